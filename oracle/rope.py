@@ -1,0 +1,46 @@
+"""Rotary position encoding at absolute positions, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+[PS] 05: positions keep counting up after eviction ("Continue PE"), so a key
+is rotated once, at the absolute position of its token, and reused as is for
+as long as it stays in the cache.
+
+The pages do not fix a rotary convention or base. The reading taken here is
+the rotate-half pairing: element i is paired with element i + D/2, and the
+pair is turned by the angle p * theta_i with theta_i = base ** (-2 i / D),
+base 10000. The angle is the float64 product of p and theta_i; cos and sin
+are float64; the rotated pair is (x c - y s, x s + y c), each product and
+sum rounded separately (no fused multiply-add).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def inv_freq(head_dim: int, base: float) -> np.ndarray:
+    """theta_i = base ** (-2 i / D) for i in [0, D/2), float64 (library pow)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * i / np.float64(head_dim))
+
+
+def angles(pos, head_dim: int, base: float) -> np.ndarray:
+    """phi[..., i] = p * theta_i in float64 for positions `pos` (any shape)."""
+    pos = np.asarray(pos, dtype=np.float64)
+    return pos[..., None] * inv_freq(head_dim, base)
+
+
+def rotate(x, pos, base: float) -> np.ndarray:
+    """Rotate vectors x[..., D] at positions pos[...] (broadcast to x's leading dims)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    phi = angles(np.broadcast_to(np.asarray(pos), x.shape[:-1]), D, base)
+    c = np.cos(phi)
+    s = np.sin(phi)
+    a = x[..., :h]
+    b = x[..., h:]
+    out = np.empty_like(x)
+    out[..., :h] = a * c - b * s
+    out[..., h:] = a * s + b * c
+    return out
