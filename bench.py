@@ -1,0 +1,225 @@
+"""Decode benchmark of prefix-pinned sliding-window attention on one MI355X.
+
+A step is one pass of the decode hot path over the batch: append the new token of every
+sequence (rotary encoding at its absolute position, ring write = eviction) and decode
+attention for it (split-KV partials over the pinned prefix and the window, then the
+cross-split merge). Inputs for every step are generated before the timed region and are
+resident in HBM when it starts; the state advances by one token per step.
+
+Default workload: bf16, 64 sequences at t = 32768, 16 query / 8 KV heads, D = 128,
+P = 100, W = 4096 (4196 visible positions per sequence).
+
+Prints one JSON line with the throughput, the roofline of the dominant kernel (the
+split-KV decode kernel, timed with HIP events on its launch stream in a separate pass)
+and the float64 CPU oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/s + achieved HBM GB/s (% peak), bf16 GQA P=100 W=4096"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "prefix_pinned_sliding_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_p100_w4096",
+                    choices=["decode_p100_w4096", "decode_p512_w16384", "ragged_decode"])
+    ap.add_argument("--t", type=int, default=0, help="override the start position t (flat-in-t sweeps)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy this many MiB with torch (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(launch_bytes_alg: float):
+    """HBM bytes per decode launch from the committed counter runs, if they were taken on
+    the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_now, q_rows, budget_s: float):
+    """Time the float64 oracle (as is) on a bounded sample of the step's sequences.
+
+    Inputs (the visible K/V rows) are generated first and are not timed. BLAS is held to
+    one thread, so the oracle runs on one core.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn
+    from synth import drive
+
+    def prepared(b):
+        full = drive.hist_provider(wl, b)
+        p = n_now[b] - 1
+        pos = np.nonzero(attn.visible_mask(wl.prefix[b], wl.window, p))[0]
+        k, v = full(pos)
+        key = pos.tobytes()
+
+        def hist(req):
+            req = np.asarray(req, dtype=np.int64)
+            assert req.tobytes() == key
+            return k, v
+        return hist
+
+    done, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while done < wl.batch and (elapsed < budget_s or done == 0):
+            b = done
+            h = prepared(b)
+            t0 = time.perf_counter()
+            attn.decode_query(q_rows[b], n_now[b] - 1, h, wl.prefix[b], wl.window,
+                              wl.n_kv_heads, wl.rope_base, wl.scale)
+            elapsed += time.perf_counter() - t0
+            done += 1
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {wl.batch} sequences of one decode step (all {wl.n_q_heads} "
+                      f"query heads, float64 NumPy, 1 thread), {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence and by KV head with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import prefix_pinned_sliding_amd as psa
+    from synth import configs, drive, gen
+
+    torch.cuda.set_device(0)
+    if args.workload == "decode_p100_w4096":
+        wl = configs.decode_p100_w4096(t=args.t) if args.t else configs.decode_p100_w4096()
+    elif args.workload == "decode_p512_w16384":
+        wl = configs.decode_p512_w16384(t=args.t) if args.t else configs.decode_p512_w16384()
+    else:
+        wl = configs.ragged_decode()
+    B = wl.batch
+    n0 = [t - 1 for t in wl.start]
+    total = args.warmup + 2 * args.steps
+    print(f"[bench] {wl.name}: filling {sum(n0)} tokens", file=sys.stderr, flush=True)
+    c = drive.make_cache(wl)
+    if args.split_tokens:
+        c.set_split_tokens(args.split_tokens)
+    drive.fill(c, wl, n0)
+
+    # inputs of every step, resident before timing
+    ks, vs, qs = [], [], []
+    for i in range(total):
+        k, v = drive.kv_block(wl, [n + i for n in n0], 1, "cuda")
+        ks.append(k)
+        vs.append(v)
+        qs.append(drive.queries(wl, [n + i for n in n0], "cuda"))
+    out = torch.empty_like(qs[0])
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready; {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr,
+          flush=True)
+
+    def step(i):
+        c.append(ks[i], vs[i])
+        c.decode(qs[i], out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_per_step = ms_total / args.steps
+    print(f"[bench] timed: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # second pass: per-kernel HIP events around each launch on the launch stream
+    c.profile(True)
+    for i in range(args.warmup + args.steps, total):
+        step(i)
+    torch.cuda.synchronize()
+    times = {name: c.profile_read(k) for k, name in psa.KERNEL_NAMES.items()}
+    c.profile(False)
+    dec_ms, dec_n = times["decode_partial"]
+    dec_avg_s = dec_ms / dec_n / 1e3
+
+    # algorithmic bytes of one decode launch: the visible K and V rows of every sequence
+    n_prof = [n + total for n in n0]          # history length during the last profiled step
+    elem = 2 if wl.dtype == torch.bfloat16 else 4
+    vis_first = wl.visible_tokens([n + args.warmup + args.steps + 1 for n in n0])
+    vis_last = wl.visible_tokens(n_prof)
+    vis = 0.5 * (vis_first + vis_last)
+    launch_bytes = vis * wl.n_kv_heads * wl.head_dim * 2 * elem
+    achieved = launch_bytes / dec_avg_s / 1e9
+    traffic = load_traffic(launch_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "prefix": wl.prefix[0] if len(set(wl.prefix)) == 1 else "ragged",
+                   "window": wl.window, "t": wl.start[0] if len(set(wl.start)) == 1 else "ragged",
+                   "visible_tokens_per_step": vis, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "decode_partial",
+                     "kernel_avg_us": dec_avg_s * 1e6, "bytes_per_launch": launch_bytes},
+        "kernels_avg_us": {k: (ms / n * 1e3 if n else None) for k, (ms, n) in times.items()},
+    }
+
+    if not args.no_cpu_baseline:
+        qc = qs[total - 1].double().cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(wl, n_prof, qc, args.cpu_seconds)
+
+    if args.copy_probe_mib:
+        nb = args.copy_probe_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: 3 x {nb} bytes", file=sys.stderr, flush=True)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * psa.h -- prefix-pinned sliding-window attention on AMD Instinct MI355X (gfx950).
+ *
+ * A bounded KV cache per sequence: a pinned prefix of P_b tokens that is never
+ * evicted, plus a fixed-length window of the last W tokens with oldest-first
+ * eviction; attention over exactly that set.
+ *
+ * Sources (cited by title and section):
+ *   [PS]      "Prefix Sliding 3倍加速", PaperDaily explainer of the Prefix Sliding
+ *             paper (longzhangge.com): 03 visible set A(t) and generation loop,
+ *             04 cost, 05 Continue PE, 06 the two-level kernel filter.
+ *   [KV-Lean] the pnsm.cn article on a Lean 4 verification of a sliding-window KV
+ *             cache: 2.2-2.4 window list model and slot positions, 3.2 cells with
+ *             positions, 3.3 step, 3.4 ring buffer read as a list, 5.1 not-full
+ *             pitfalls, 6.3 export-and-compare checks.
+ *
+ * Conventions used by every call:
+ *   - Positions are 0-based absolute token positions p (p = t - 1 for the pages'
+ *     1-based t). A sequence's history length n counts every token appended so far.
+ *   - The query at position p attends to key j iff j <= p and (j < P_b or
+ *     j >= p - W + 1): the pinned prefix [1, P] and the window
+ *     [max(P + 1, t - W + 1), t] of [PS] 03. A query inside the prefix (p < P_b)
+ *     attends causally to [0, p].
+ *   - Keys are rotated (rotary position encoding, rotate-half pairing (i, i + D/2),
+ *     theta_i = rope_base^(-2i/D)) at their absolute position once, when appended,
+ *     and reused as stored ([PS] 05, "Continue PE"). The rotation is computed in
+ *     float64 and rounded once (nearest, ties to even) to the storage dtype.
+ *   - Grouped-query heads: query head hq reads KV head hq / (n_q_heads / n_kv_heads).
+ *   - Tensors are dense, row-major, in the cache dtype unless stated otherwise.
+ *   - Every device pointer is caller-owned device memory on the cache's device;
+ *     the library never allocates or frees device memory. Host pointers are
+ *     caller-owned host memory.
+ *   - Calls taking a stream enqueue work on it and return without waiting, except
+ *     psa_cache_create and psa_export, which wait for the stream. The caller
+ *     serialises calls on one handle (a handle is not thread-safe). Calls on one
+ *     cache must be issued on one stream (or ordered by the caller).
+ *   - Errors: every argument and state error is detected on the host before any
+ *     work is enqueued, and leaves the cache unchanged. PSA_ERR_HIP reports a
+ *     failed HIP runtime call or launch; psa_last_error() gives the text.
+ */
+#ifndef PSA_H
+#define PSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque host handle, owned by the library (psa_cache_create / psa_cache_destroy). */
+typedef struct psa_cache psa_cache;
+
+/* A hipStream_t passed as a plain pointer; NULL is the null stream. */
+typedef void *psa_stream;
+
+/* Status codes. */
+enum {
+    PSA_OK = 0,
+    PSA_ERR_ARG = 1,      /* invalid argument: null pointer, unsupported shape or dtype, size */
+    PSA_ERR_STATE = 2,    /* operation not valid in the cache's current state */
+    PSA_ERR_OVERFLOW = 3, /* a sequence length would exceed INT32_MAX */
+    PSA_ERR_HIP = 4       /* a HIP runtime call or kernel launch failed */
+};
+
+/* Storage / input dtype. */
+enum { PSA_BF16 = 0, PSA_F32 = 1 };
+
+/* Cache description. */
+typedef struct {
+    int32_t max_batch;   /* number of sequences B >= 1 */
+    int32_t n_q_heads;   /* H_q >= 1, a multiple of n_kv_heads, H_q / H_kv in {1, 2, 4, 8} */
+    int32_t n_kv_heads;  /* H_kv >= 1 */
+    int32_t head_dim;    /* D: 64 or 128 */
+    int32_t prefix_max;  /* P_max >= 0: largest pinned-prefix length any sequence may use */
+    int32_t window;      /* W >= 1: window length */
+    int32_t dtype;       /* PSA_BF16 or PSA_F32 (storage, inputs and outputs) */
+    int32_t max_chunk;   /* largest prefill chunk C (0: psa_prefill_attn unavailable) */
+    double rope_base;    /* > 0, e.g. 10000 */
+    float scale;         /* softmax scale; 0 selects 1 / sqrt(head_dim) */
+    int32_t reserved;    /* must be 0 */
+} psa_cache_desc;
+
+/* Byte offsets of the regions the library carves out of the caller's device buffer.
+ * K and V: [B][H_kv][S][D] with S = prefix_max + window slots per (sequence, head):
+ * slots [0, P_max) hold prefix positions p < P_b at slot p; slots [P_max, S) are the
+ * ring, position p >= P_b at slot P_max + (p - P_b) mod W.
+ * tags: [B][S] int32, the absolute position held by each slot, -1 if never written. */
+typedef struct {
+    size_t k_offset;
+    size_t v_offset;
+    size_t tags_offset;
+    size_t state_offset;  /* library-private per-sequence state */
+    size_t work_offset;   /* library-private workspace */
+    size_t total_bytes;   /* == psa_cache_bytes() */
+    int32_t slots;        /* S */
+    int32_t elem_bytes;   /* 2 (bf16) or 4 (f32) */
+} psa_layout;
+
+/* Device bytes the caller must provide for a cache described by *desc (0 if *desc is
+ * invalid; psa_last_error() then says why). Host only; enqueues nothing. */
+size_t psa_cache_bytes(const psa_cache_desc *desc);
+
+/* Fill *out with the layout of a cache described by *desc. Host only.
+ * Returns PSA_ERR_ARG for a null pointer or an invalid description. */
+int psa_cache_layout(const psa_cache_desc *desc, psa_layout *out);
+
+/* Create a cache over caller-owned device memory dev_mem (>= psa_cache_bytes(desc)
+ * bytes, 256-byte aligned) on the current HIP device. Initialises every slot tag to
+ * -1 and every sequence to "not started", then waits for `stream`.
+ * On success *out receives a new handle; on error *out is left unchanged.
+ * The memory stays owned by the caller and must outlive the handle. */
+int psa_cache_create(const psa_cache_desc *desc, void *dev_mem, size_t bytes, psa_stream stream,
+                     psa_cache **out);
+
+/* Release the host handle (the device memory is the caller's). NULL is accepted. */
+int psa_cache_destroy(psa_cache *cache);
+
+/* Start (or restart) sequence `seq` with a pinned prefix of prefix_len tokens
+ * (0 <= prefix_len <= prefix_max; 0 gives the plain sliding window). Its history
+ * becomes empty and all its slot tags -1. The prefix is the first prefix_len tokens
+ * appended afterwards ([PS] 03: the prefix KV is encoded once and never evicted). */
+int psa_seq_reset(psa_cache *cache, int32_t seq, int32_t prefix_len, psa_stream stream);
+
+/* Append new tokens to every sequence ([PS] 03 generation loop; [KV-Lean] 2.2, 3.3:
+ * append at the tail, evict the oldest once the window holds more than W).
+ * k, v: [B][n_stride][H_kv][D]. Sequence b appends n_b tokens, rows 0 .. n_b - 1 of
+ * its block, at positions len_b, len_b + 1, ...: n_b = n_new_host[b] if n_new_host is
+ * not NULL (a host array of B entries), else n_uniform. 0 <= n_b <= n_stride.
+ * A token at p < P_b goes to prefix slot p; otherwise to ring slot (p - P_b) mod W,
+ * overwriting (evicting) position p - W. The key is stored rotated at p. A token that
+ * a later token of the same call evicts is not written.
+ * Errors: PSA_ERR_STATE if a sequence with n_b > 0 was never reset;
+ * PSA_ERR_OVERFLOW if len_b + n_b > INT32_MAX. */
+int psa_append(psa_cache *cache, const int32_t *n_new_host, int32_t n_uniform, const void *k,
+               const void *v, int32_t n_stride, psa_stream stream);
+
+/* Decode attention for every sequence ([PS] 03 visible set; [PS] 06: only prefix and
+ * window blocks are read). The query of sequence b is the token at p = len_b - 1,
+ * i.e. the one most recently appended; it sees the prefix and the window, itself
+ * included. q, out: [B][H_q][D]; lse: [B][H_q] float32 natural-log log-sum-exp of the
+ * scaled logits, or NULL. Errors: PSA_ERR_STATE if any sequence is empty. */
+int psa_decode_attn(psa_cache *cache, const void *q, void *out, float *lse, psa_stream stream);
+
+/* Chunked prefill: every sequence takes `chunk` new tokens at positions
+ * len_b .. len_b + chunk - 1; query row c (at p = len_b + c) attends to the prefix,
+ * the window of p and the chunk's own tokens up to p (a chunk equals `chunk`
+ * consecutive decode steps). Then the chunk is appended as by psa_append.
+ * q, out: [B][chunk][H_q][D]; k, v: [B][chunk][H_kv][D]; lse: [B][chunk][H_q] float32
+ * or NULL. 1 <= chunk <= max_chunk. Errors: PSA_ERR_STATE if a sequence was never
+ * reset; PSA_ERR_OVERFLOW as psa_append. */
+int psa_prefill_attn(psa_cache *cache, int32_t chunk, const void *q, const void *k,
+                     const void *v, void *out, float *lse, psa_stream stream);
+
+/* Copy sequence `seq`'s logical cache to host memory ([KV-Lean] 3.4 ring read back
+ * as a list; 6.3 export and compare against the list model): the prefix entries,
+ * then the window oldest first, count = min(len, P_b + W) entries. k_host, v_host:
+ * [S][H_kv][D] (S = prefix_max + window entries of capacity), pos_host: [S] int32
+ * absolute positions; any of the three may be NULL. Waits for `stream`. */
+int psa_export(psa_cache *cache, int32_t seq, void *k_host, void *v_host, int32_t *pos_host,
+               int32_t *count, psa_stream stream);
+
+/* History length of `seq` from the host mirror (-1 if seq is out of range or the
+ * sequence was never reset). Host only. */
+int64_t psa_seq_length(const psa_cache *cache, int32_t seq);
+
+/* Tokens per decode split (work unit of one workgroup); 0 restores the automatic
+ * choice. Must be 0 or a multiple of 128. Results are the same up to float32
+ * rounding order for any value. Host only. */
+int psa_set_split_tokens(psa_cache *cache, int32_t tokens);
+
+/* Kernel timing with HIP events recorded on the launch stream around each kernel.
+ * enable != 0 starts recording (and clears earlier totals), 0 stops it. */
+int psa_profile(psa_cache *cache, int32_t enable);
+
+/* Kernel ids for psa_profile_read. */
+enum {
+    PSA_K_APPEND = 0,        /* ring append with RoPE */
+    PSA_K_DECODE = 1,        /* split-KV decode partials */
+    PSA_K_MERGE = 2,         /* cross-split log-sum-exp merge */
+    PSA_K_PREFILL_STAGE = 3, /* rotate a prefill chunk's keys */
+    PSA_K_PREFILL = 4,       /* chunked-prefill attention */
+    PSA_K_COUNT = 5
+};
+
+/* Waits for the recorded events, then gives the summed duration in milliseconds and
+ * the number of launches of kernel `kernel` since profiling was enabled. */
+int psa_profile_read(psa_cache *cache, int32_t kernel, double *total_ms, int64_t *launches);
+
+/* Static text of a status code. */
+const char *psa_status_string(int status);
+
+/* Text of the last error on this thread (empty if none). */
+const char *psa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_H */

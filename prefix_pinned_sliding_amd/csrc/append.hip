@@ -1,0 +1,222 @@
+// Ring append with rotary encoding at the absolute position (K1), the fills used by
+// cache creation and sequence reset, and the staging rotation of a prefill chunk.
+//
+// [PS] 03 generation loop: the prefix KV is kept for good, each new token joins the
+// window, and the window drops its oldest token once it holds more than W.
+// [PS] 05 Continue PE: positions keep counting up, so a key is rotated once, at its
+// absolute position, and reused unchanged while it stays cached.
+// [KV-Lean] 3.2: every slot carries the absolute position of the token it holds.
+#include "psa_internal.h"
+
+namespace psa {
+namespace {
+
+constexpr int kBlock = 256;
+
+// Storage element types: bf16 is kept as raw 16-bit patterns.
+template <int DT> struct Elem;
+template <> struct Elem<PSA_BF16> { using T = uint16_t; };
+template <> struct Elem<PSA_F32> { using T = float; };
+
+__device__ __forceinline__ double to_f64(uint16_t b) {
+    return (double)__uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ double to_f64(float f) { return (double)f; }
+
+// float64 -> bfloat16 bits, one rounding to nearest, ties to even, on the float64 bit
+// fields: results below 2^-126 become bfloat16 subnormals, a carry out of the
+// fraction bumps the exponent, overflow gives infinity, NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+    const int e = (int)((u >> 52) & 0x7FF);
+    const uint64_t frac = u & ((1ull << 52) - 1);
+    if (e == 0x7FF) return sign | (frac ? 0x7FC0 : 0x7F80);
+    if (e == 0) return sign;                       // float64 zero or subnormal
+    const int E = e - 1023;
+    if (E >= -126) {
+        uint64_t body = ((uint64_t)(E + 127) << 7) | (frac >> 45);
+        const uint64_t rem = frac & ((1ull << 45) - 1);
+        const uint64_t half = 1ull << 44;
+        if (rem > half || (rem == half && (body & 1ull))) ++body;
+        if (body >= 0x7F80ull) body = 0x7F80ull;
+        return sign | (uint16_t)body;
+    }
+    const int sh = -E - 81;                        // leaves units of 2^-133
+    if (sh >= 64) return sign;
+    const uint64_t full = frac | (1ull << 52);
+    uint64_t kept = full >> sh;
+    const uint64_t rem = full & ((1ull << sh) - 1);
+    const uint64_t half = 1ull << (sh - 1);
+    if (rem > half || (rem == half && (kept & 1ull))) ++kept;
+    return sign | (uint16_t)kept;
+}
+
+__device__ __forceinline__ uint16_t store_as(double x, uint16_t*) { return f64_to_bf16(x); }
+__device__ __forceinline__ float store_as(double x, float*) { return (float)x; }
+
+// Rotate the pair (x, y) by the angle p * theta in float64: (x c - y s, x s + y c), each
+// product and sum rounded on its own.
+__device__ __forceinline__ void rotate_pair(double x, double y, int p, double theta, double* xr,
+                                            double* yr) {
+#pragma clang fp contract(off)
+    const double phi = (double)p * theta;
+    double sn, cs;
+    sincos(phi, &sn, &cs);
+    const double a = x * cs;
+    const double b = y * sn;
+    const double c = x * sn;
+    const double d = y * cs;
+    *xr = a - b;
+    *yr = c + d;
+}
+
+__global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_state) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n_tags) tags[i] = -1;
+    if (i < (size_t)n_state) state[i] = 0;
+}
+
+__global__ void seq_reset_kernel(int32_t* tags, int S, int32_t* len_cur, int32_t* pre, int seq,
+                                 int prefix_len) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < S) tags[(size_t)seq * S + i] = -1;
+    if (i == 0) {
+        len_cur[seq] = 0;
+        pre[seq] = prefix_len;
+    }
+}
+
+// One thread per (sequence b, token j, kv head h, rotation pair i). Token j of sequence b
+// has position p = len[b] + j. Slot: p < P_b -> prefix slot p; else ring slot
+// P_max + (p - P_b) mod W. A ring token that a later token of the same call overwrites
+// (p < len[b] + n_b - W) is not written, so the surviving writer of each slot is unique.
+template <int DT, int D>
+__global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typename Elem<DT>::T* k,
+                                                        const typename Elem<DT>::T* v, int n_stride,
+                                                        int n_uniform, int ragged, int k_rotated,
+                                                        const int32_t* __restrict__ len_cur,
+                                                        int32_t* __restrict__ len_next) {
+    using T = typename Elem<DT>::T;
+    constexpr int H = D / 2;
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t total = (size_t)c.B * n_stride * c.Hkv * H;
+    if (idx >= total) return;
+    const int i = (int)(idx % H);
+    size_t r = idx / H;
+    const int h = (int)(r % c.Hkv);
+    r /= c.Hkv;
+    const int j = (int)(r % n_stride);
+    const int b = (int)(r / n_stride);
+
+    const int nb = ragged ? c.nnew[b] : n_uniform;
+    const int L0 = len_cur[b];
+    if (j == 0 && h == 0 && i == 0) len_next[b] = L0 + nb;
+    if (j >= nb) return;
+
+    const int p = L0 + j;
+    const int P = c.pre[b];
+    int slot;
+    if (p < P) {
+        slot = p;
+    } else {
+        if (p < L0 + nb - c.W) return;             // evicted by a later token of this call
+        slot = c.Pmax + (p - P) % c.W;
+    }
+    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * D;
+    const size_t dst = (((size_t)b * c.Hkv + h) * c.S + slot) * D;
+    T* K = (T*)c.k;
+    T* V = (T*)c.v;
+    if (k_rotated) {
+        K[dst + i] = k[src + i];
+        K[dst + i + H] = k[src + i + H];
+    } else {
+        double xr, yr;
+        rotate_pair(to_f64(k[src + i]), to_f64(k[src + i + H]), p, c.inv_freq[i], &xr, &yr);
+        K[dst + i] = store_as(xr, (T*)nullptr);
+        K[dst + i + H] = store_as(yr, (T*)nullptr);
+    }
+    V[dst + i] = v[src + i];
+    V[dst + i + H] = v[src + i + H];
+    if (h == 0 && i == 0) c.tags[(size_t)b * c.S + slot] = p;
+}
+
+// Rotate a prefill chunk's keys into the staging buffer: stage[b][j][h][:] holds
+// RNE(rotate(k[b][j][h][:], len[b] + j)), the exact bytes the append will store.
+template <int DT, int D>
+__global__ __launch_bounds__(kBlock) void stage_kernel(DevCache c, const typename Elem<DT>::T* k,
+                                                       int chunk,
+                                                       const int32_t* __restrict__ len_cur) {
+    using T = typename Elem<DT>::T;
+    constexpr int H = D / 2;
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t total = (size_t)c.B * chunk * c.Hkv * H;
+    if (idx >= total) return;
+    const int i = (int)(idx % H);
+    size_t r = idx / H;
+    const int h = (int)(r % c.Hkv);
+    r /= c.Hkv;
+    const int j = (int)(r % chunk);
+    const int b = (int)(r / chunk);
+    const int p = len_cur[b] + j;
+    const size_t off = (((size_t)b * chunk + j) * c.Hkv + h) * D;
+    double xr, yr;
+    rotate_pair(to_f64(k[off + i]), to_f64(k[off + i + H]), p, c.inv_freq[i], &xr, &yr);
+    T* out = (T*)c.stage_k;
+    out[off + i] = store_as(xr, (T*)nullptr);
+    out[off + i + H] = store_as(yr, (T*)nullptr);
+}
+
+inline unsigned blocks_for(size_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
+
+}  // namespace
+
+hipError_t launch_init(const DevCache& c, hipStream_t s) {
+    const size_t n_tags = (size_t)c.B * c.S;
+    const int n_state = 4 * c.B;   // len[0], len[1], pre, nnew are contiguous
+    const size_t n = n_tags > (size_t)n_state ? n_tags : (size_t)n_state;
+    hipLaunchKernelGGL(init_kernel, dim3(blocks_for(n)), dim3(kBlock), 0, s, c.tags, n_tags,
+                       c.len[0], n_state);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int cur, hipStream_t s) {
+    hipLaunchKernelGGL(seq_reset_kernel, dim3(blocks_for((size_t)c.S)), dim3(kBlock), 0, s, c.tags,
+                       c.S, c.len[cur], c.pre, seq, prefix_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_stride,
+                         int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s) {
+    const size_t total = (size_t)c.B * n_stride * c.Hkv * (c.D / 2);
+    const dim3 grid(blocks_for(total));
+#define PSA_APPEND(DT, DD)                                                                     \
+    hipLaunchKernelGGL((append_kernel<DT, DD>), grid, dim3(kBlock), 0, s, c,                   \
+                       (const typename Elem<DT>::T*)k, (const typename Elem<DT>::T*)v, n_stride, \
+                       n_uniform, ragged, k_rotated, c.len[cur], c.len[cur ^ 1])
+    if (c.dtype == PSA_BF16) {
+        if (c.D == 128) PSA_APPEND(PSA_BF16, 128); else PSA_APPEND(PSA_BF16, 64);
+    } else {
+        if (c.D == 128) PSA_APPEND(PSA_F32, 128); else PSA_APPEND(PSA_F32, 64);
+    }
+#undef PSA_APPEND
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur,
+                                hipStream_t s) {
+    const size_t total = (size_t)c.B * chunk * c.Hkv * (c.D / 2);
+    const dim3 grid(blocks_for(total));
+#define PSA_STAGE(DT, DD)                                                                       \
+    hipLaunchKernelGGL((stage_kernel<DT, DD>), grid, dim3(kBlock), 0, s, c,                     \
+                       (const typename Elem<DT>::T*)k, chunk, c.len[cur])
+    if (c.dtype == PSA_BF16) {
+        if (c.D == 128) PSA_STAGE(PSA_BF16, 128); else PSA_STAGE(PSA_BF16, 64);
+    } else {
+        if (c.D == 128) PSA_STAGE(PSA_F32, 128); else PSA_STAGE(PSA_F32, 64);
+    }
+#undef PSA_STAGE
+    return hipGetLastError();
+}
+
+}  // namespace psa

@@ -1,0 +1,357 @@
+// Split-KV decode attention over the pinned prefix and the window (K2) and the
+// cross-split log-sum-exp merge (K3).
+//
+// [PS] 03: the query at t sees [1, P] and [max(P + 1, t - W + 1), t]. After the token at
+// p = n - 1 is appended, the cache holds exactly that set: prefix slots [0, min(n, P_b))
+// and the first min(W, n - P_b) ring slots. [PS] 06 skips every block of the evicted
+// middle; here the middle is never in memory, so the walk covers two contiguous slot
+// ranges and nothing else, and the only partially covered tile is the last one of a
+// split (masked per key). Softmax order does not matter, so the ring is walked in slot
+// order rather than age order.
+//
+// Work split: one workgroup (4 waves) per (split, kv head, sequence). A split is a
+// contiguous run of `split_tokens` entries of the concatenated [prefix | ring] list.
+// Within a wave, LPK lanes share one key (each holds D / LPK of its elements, 16-byte
+// loads), so a wave covers 64 / LPK keys per load; the G query heads of the kv head
+// reuse every K/V element loaded. Logits are reduced over the LPK lanes with DPP, the
+// softmax reference max is kept per wave (rescaling only when a tile max exceeds it by
+// more than 2^8), and partial sums are combined across lane groups and waves once per
+// split. K3 then merges the splits of each (sequence, query head).
+#include "psa_internal.h"
+
+namespace psa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBlock = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;   // log2-domain headroom before a rescale
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Elem;
+template <> struct Elem<PSA_BF16> { using T = uint16_t; };
+template <> struct Elem<PSA_F32> { using T = float; };
+
+__device__ __forceinline__ double to_f64(uint16_t b) {
+    return (double)__uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ double to_f64(float f) { return (double)f; }
+
+// Unpack one 16-byte chunk into floats.
+__device__ __forceinline__ void unpack(const u32x4& w, float* f, uint16_t*) {
+    f[0] = __uint_as_float(w.x << 16); f[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(w.y << 16); f[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(w.z << 16); f[5] = __uint_as_float(w.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(w.w << 16); f[7] = __uint_as_float(w.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void unpack(const u32x4& w, float* f, float*) {
+    f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+
+// float32 -> bfloat16 bits, nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t out_as(float x, uint16_t*) { return f32_to_bf16(x); }
+__device__ __forceinline__ float out_as(float x, float*) { return x; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                              0xF, 0xF, false));
+}
+
+// Sum over the LPK consecutive lanes that share a key (result in all of them).
+template <int LPK>
+__device__ __forceinline__ float key_sum(float x) {
+    x += dpp<0xB1>(x);                               // quad_perm [1,0,3,2]
+    if constexpr (LPK >= 4) x += dpp<0x4E>(x);       // quad_perm [2,3,0,1]
+    if constexpr (LPK >= 8) x += dpp<0x141>(x);      // row_half_mirror
+    if constexpr (LPK >= 16) x += dpp<0x140>(x);     // row_mirror
+    return x;
+}
+
+// Max over the whole wave of a value replicated within each LPK-lane group.
+template <int LPK>
+__device__ __forceinline__ float wave_max(float x) {
+    if constexpr (LPK < 8) x = fmaxf(x, dpp<0x124>(x));    // row_ror:4
+    if constexpr (LPK < 16) x = fmaxf(x, dpp<0x128>(x));   // row_ror:8
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+// Sum within a 16-lane row over the lane groups that hold the same elements.
+template <int LPK>
+__device__ __forceinline__ float row_group_sum(float x) {
+    if constexpr (LPK < 8) x += dpp<0x124>(x);      // row_ror:4
+    if constexpr (LPK < 16) x += dpp<0x128>(x);     // row_ror:8
+    return x;
+}
+
+template <int DT, int D, int G, int LPK>
+__global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
+                                                                const typename Elem<DT>::T* q,
+                                                                int split_tokens,
+                                                                const int32_t* __restrict__ len_cur) {
+    using T = typename Elem<DT>::T;
+    constexpr int EPC = 16 / (int)sizeof(T);    // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;                // chunks per row
+    constexpr int CPL = CPR / LPK;              // chunks per lane
+    constexpr int EPL = CPL * EPC;              // elements per lane
+    constexpr int KPW = 64 / LPK;               // keys per wave per load round
+    constexpr int U = 2;                        // load rounds per iteration
+    constexpr int ROWS = 4;                     // 16-lane rows per wave
+    static_assert(CPL >= 1 && CPR % LPK == 0, "lane layout");
+
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int n = len_cur[b];
+    const int P = c.pre[b];
+    const int n_pre = min(n, P);
+    const int n_win = min(c.W, max(0, n - P));
+    const int Tb = n_pre + n_win;
+    const int ns = (Tb + split_tokens - 1) / split_tokens;
+    if (split >= ns) return;
+    const int i0 = split * split_tokens;
+    const int i1 = min(Tb, i0 + split_tokens);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = lane % LPK, grp = lane / LPK;
+
+    __shared__ float q_s[G][D];
+    __shared__ float red_o[kWaves][ROWS][G][D];
+    __shared__ float red_l[kWaves][ROWS][G];
+    __shared__ float red_m[kWaves][G];
+
+    // Query heads h*G .. h*G+G-1 rotated at p = n - 1 (float64 angle and rotation), then
+    // scaled by scale * log2(e) so the softmax runs on exp2.
+    {
+        const int p = n - 1;
+        const float sc = c.scale * kLog2e;
+        for (int idx = tid; idx < G * (D / 2); idx += kBlock) {
+            const int g = idx / (D / 2), i = idx % (D / 2);
+            const T* qp = q + ((size_t)b * c.Hq + h * G + g) * D;
+            const double x = to_f64(qp[i]), y = to_f64(qp[i + D / 2]);
+            double sn, cs;
+            sincos((double)p * c.inv_freq[i], &sn, &cs);
+            q_s[g][i] = (float)(x * cs - y * sn) * sc;
+            q_s[g][i + D / 2] = (float)(x * sn + y * cs) * sc;
+        }
+    }
+    __syncthreads();
+
+    float qr[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) qr[g][cc * EPC + e] = q_s[g][(cc * LPK + sub) * EPC + e];
+
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+
+    const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
+    const T* Kb = (const T*)c.k + head_off;
+    const T* Vb = (const T*)c.v + head_off;
+
+    for (int base_i = i0 + wave * KPW * U; base_i < i1; base_i += kWaves * KPW * U) {
+        u32x4 kw[U][CPL], vw[U][CPL];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base_i + u * KPW + grp;
+            ok[u] = i < i1;
+            const int ii = ok[u] ? i : i1 - 1;
+            const int slot = ii < n_pre ? ii : c.Pmax + (ii - n_pre);
+            const u32x4* kp = reinterpret_cast<const u32x4*>(Kb + (size_t)slot * D);
+            const u32x4* vp = reinterpret_cast<const u32x4*>(Vb + (size_t)slot * D);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                kw[u][cc] = __builtin_nontemporal_load(kp + cc * LPK + sub);
+                vw[u][cc] = __builtin_nontemporal_load(vp + cc * LPK + sub);
+            }
+        }
+        float s[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[EPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) unpack(kw[u][cc], kf + cc * EPC, (T*)nullptr);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d += qr[g][e] * kf[e];
+                d = key_sum<LPK>(d);
+                s[u][g] = ok[u] ? d : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float mt = s[0][g];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+            mt = wave_max<LPK>(mt);
+            if (mt > m[g] + kRescaleSlack) {          // wave-uniform
+                const float f = __builtin_amdgcn_exp2f(m[g] - mt);
+                l[g] *= f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+                m[g] = mt;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) unpack(vw[u][cc], vf + cc * EPC, (T*)nullptr);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float pr = __builtin_amdgcn_exp2f(s[u][g] - m[g]);
+                l[g] += pr;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] += pr * vf[e];
+            }
+        }
+    }
+
+    // Combine: lane groups in a row share m, so sum them; rows and waves go through LDS.
+    const int row = lane >> 4;
+    const bool row_leader = (lane & 15) < LPK;      // first group of each row
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float lg = row_group_sum<LPK>(l[g]);
+        if ((lane & 15) == 0) red_l[wave][row][g] = lg;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                const float a = row_group_sum<LPK>(acc[g][cc * EPC + e]);
+                if (row_leader) red_o[wave][row][g][(cc * LPK + sub) * EPC + e] = a;
+            }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) red_m[wave][g] = m[g];
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < G * D; idx += kBlock) {
+        const int g = idx / D, d = idx % D;
+        float M = red_m[0][g];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w][g]);
+        float o = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = __builtin_amdgcn_exp2f(red_m[w][g] - M);   // 0 for an idle wave
+            float ow = 0.f, lw = 0.f;
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                ow += red_o[w][r][g][d];
+                lw += red_l[w][r][g];
+            }
+            o += f * ow;
+            L += f * lw;
+        }
+        const size_t hq = (size_t)b * c.Hq + h * G + g;
+        const size_t part = hq * c.max_splits + split;
+        c.part_o[part * D + d] = o;
+        if (d == 0) {
+            c.part_ml[part * 2 + 0] = M;
+            c.part_ml[part * 2 + 1] = L;
+        }
+    }
+}
+
+// Merge the splits of one (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
+// out = sum O_s 2^(m_s - M) / L, rounded once to the output dtype; lse = (M + log2 L) ln 2.
+template <int DT, int D>
+__global__ __launch_bounds__(D) void merge_kernel(DevCache c, typename Elem<DT>::T* out,
+                                                  float* lse, int split_tokens,
+                                                  const int32_t* __restrict__ len_cur) {
+    using T = typename Elem<DT>::T;
+    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int n = len_cur[b];
+    const int P = c.pre[b];
+    const int Tb = min(n, P) + min(c.W, max(0, n - P));
+    const int ns = (Tb + split_tokens - 1) / split_tokens;
+    const size_t base = ((size_t)b * c.Hq + hq) * c.max_splits;
+    const float* ml = c.part_ml + base * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.f, o = 0.f;
+    for (int s = 0; s < ns; ++s) {
+        const float f = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+        L += ml[2 * s + 1] * f;
+        o += c.part_o[(base + s) * D + d] * f;
+    }
+    out[((size_t)b * c.Hq + hq) * D + d] = out_as(o / L, (T*)nullptr);
+    if (lse != nullptr && d == 0) lse[(size_t)b * c.Hq + hq] = (M + __log2f(L)) * kLn2;
+}
+
+template <int DT, int D, int G>
+hipError_t launch_partial_g(const DevCache& c, const void* q, int split_tokens, int grid_splits,
+                            int cur, hipStream_t s) {
+    // Lanes per key: enough that q and the accumulators of G heads fit in registers,
+    // never more than the 16-byte chunks in a row.
+    constexpr int CPR = D / (16 / (int)sizeof(typename Elem<DT>::T));
+    constexpr int PREF = G <= 2 ? 4 : (G == 4 ? 8 : 16);
+    constexpr int LPK = PREF < CPR ? PREF : CPR;
+    const dim3 grid(grid_splits, c.Hkv, c.B);
+    hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK>), grid, dim3(kBlock), 0, s, c,
+                       (const typename Elem<DT>::T*)q, split_tokens, c.len[cur]);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_partial_d(const DevCache& c, const void* q, int split_tokens, int grid_splits,
+                            int cur, hipStream_t s) {
+    switch (c.Hq / c.Hkv) {
+        case 1: return launch_partial_g<DT, D, 1>(c, q, split_tokens, grid_splits, cur, s);
+        case 2: return launch_partial_g<DT, D, 2>(c, q, split_tokens, grid_splits, cur, s);
+        case 4: return launch_partial_g<DT, D, 4>(c, q, split_tokens, grid_splits, cur, s);
+        default: return launch_partial_g<DT, D, 8>(c, q, split_tokens, grid_splits, cur, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
+                                 int grid_splits, int cur, hipStream_t s) {
+    if (c.dtype == PSA_BF16)
+        return c.D == 128 ? launch_partial_d<PSA_BF16, 128>(c, q, split_tokens, grid_splits, cur, s)
+                          : launch_partial_d<PSA_BF16, 64>(c, q, split_tokens, grid_splits, cur, s);
+    return c.D == 128 ? launch_partial_d<PSA_F32, 128>(c, q, split_tokens, grid_splits, cur, s)
+                      : launch_partial_d<PSA_F32, 64>(c, q, split_tokens, grid_splits, cur, s);
+}
+
+hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,
+                        hipStream_t s) {
+    const dim3 grid(c.Hq, c.B);
+#define PSA_MERGE(DT, DD)                                                                     \
+    hipLaunchKernelGGL((merge_kernel<DT, DD>), grid, dim3(DD), 0, s, c,                       \
+                       (typename Elem<DT>::T*)out, lse, split_tokens, c.len[cur])
+    if (c.dtype == PSA_BF16) {
+        if (c.D == 128) PSA_MERGE(PSA_BF16, 128); else PSA_MERGE(PSA_BF16, 64);
+    } else {
+        if (c.D == 128) PSA_MERGE(PSA_F32, 128); else PSA_MERGE(PSA_F32, 64);
+    }
+#undef PSA_MERGE
+    return hipGetLastError();
+}
+
+}  // namespace psa

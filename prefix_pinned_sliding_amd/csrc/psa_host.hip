@@ -1,0 +1,467 @@
+// C-ABI entry points of libpsa: argument and state validation, layout of the caller's
+// device buffer, the host mirror of sequence lengths and prefix lengths, decode split
+// planning, export of the logical cache view, and optional per-kernel event timing.
+// All device work is done by the kernels in append.hip, decode.hip and prefill.hip.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "psa_internal.h"
+
+#define PSA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const std::string& msg) {
+    g_err = msg;
+    return status;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct EventPair {
+    int kernel;
+    hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct psa_cache {
+    psa_cache_desc desc;
+    psa::Layout L;
+    psa::DevCache dev;
+    int device;
+    int cur;                       // which device length buffer is current
+    std::vector<int64_t> len;      // host mirror of history lengths
+    std::vector<int32_t> pre;      // host mirror of P_b; -1 = never reset
+    int32_t split_tokens;          // 0 = automatic
+    bool profiling;
+    std::vector<EventPair> pending;
+    double total_ms[PSA_K_COUNT];
+    int64_t launches[PSA_K_COUNT];
+};
+
+namespace psa {
+
+bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
+    auto bad = [&](const char* w) {
+        *why = w;
+        return false;
+    };
+    if (d.max_batch < 1) return bad("max_batch must be >= 1");
+    if (d.n_kv_heads < 1) return bad("n_kv_heads must be >= 1");
+    if (d.n_q_heads < 1 || d.n_q_heads % d.n_kv_heads != 0)
+        return bad("n_q_heads must be a positive multiple of n_kv_heads");
+    const int G = d.n_q_heads / d.n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return bad("n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+    if (d.head_dim != 64 && d.head_dim != 128) return bad("head_dim must be 64 or 128");
+    if (d.prefix_max < 0) return bad("prefix_max must be >= 0");
+    if (d.window < 1) return bad("window must be >= 1");
+    if (d.dtype != PSA_BF16 && d.dtype != PSA_F32) return bad("dtype must be PSA_BF16 or PSA_F32");
+    if (d.max_chunk < 0) return bad("max_chunk must be >= 0");
+    if (!(d.rope_base > 0.0) || !isfinite(d.rope_base)) return bad("rope_base must be finite and > 0");
+    if (!(d.scale >= 0.f) || !isfinite(d.scale)) return bad("scale must be finite and >= 0");
+    if (d.reserved != 0) return bad("reserved must be 0");
+    const int64_t S = (int64_t)d.prefix_max + d.window;
+    if (S > (1 << 30)) return bad("prefix_max + window too large");
+    const size_t elem = d.dtype == PSA_BF16 ? 2 : 4;
+    const size_t B = (size_t)d.max_batch, Hq = (size_t)d.n_q_heads, Hkv = (size_t)d.n_kv_heads;
+    const size_t D = (size_t)d.head_dim;
+    const int64_t max_splits = (S + kSplitGranule - 1) / kSplitGranule;
+    const size_t A = 256;
+    size_t off = 0;
+    L->k = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
+    L->v = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
+    L->tags = off;     off = align_up(off + B * (size_t)S * 4, A);
+    L->state = off;    off = align_up(off + 4 * B * 4, A);
+    L->inv_freq = off; off = align_up(off + D / 2 * 8, A);
+    L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
+    L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
+    L->stage_k = off;  off = align_up(off + B * (size_t)d.max_chunk * Hkv * D * elem, A);
+    L->total = off;
+    L->S = (int32_t)S;
+    L->elem = (int32_t)elem;
+    L->max_splits = (int32_t)max_splits;
+    return true;
+}
+
+}  // namespace psa
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Launch bracketed by timing events when profiling is on.
+template <typename F>
+int timed(psa_cache* c, int kernel, hipStream_t s, const char* what, F&& launch) {
+    EventPair ev{kernel, nullptr, nullptr};
+    if (c->profiling) {
+        hipError_t e = hipEventCreate(&ev.start);
+        if (e == hipSuccess) e = hipEventCreate(&ev.stop);
+        if (e == hipSuccess) e = hipEventRecord(ev.start, s);
+        if (e != hipSuccess) return hip_fail(e, "profiling event");
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (c->profiling) {
+        const hipError_t e2 = hipEventRecord(ev.stop, s);
+        if (e2 != hipSuccess) return hip_fail(e2, "profiling event");
+        c->pending.push_back(ev);
+    }
+    return PSA_OK;
+}
+
+// Visible entries of sequence b: min(n, P_b) prefix entries plus min(W, n - P_b) window entries.
+int64_t visible_count(const psa_cache* c, int b) {
+    const int64_t n = c->len[b], P = c->pre[b];
+    const int64_t n_pre = n < P ? n : P;
+    int64_t n_win = n - P;
+    if (n_win < 0) n_win = 0;
+    if (n_win > c->desc.window) n_win = c->desc.window;
+    return n_pre + n_win;
+}
+
+// Automatic split length: the smallest multiple of 256 that keeps the decode grid at or
+// below about 16 workgroups per compute unit of work, but no shorter than 256 tokens.
+int auto_split_tokens(const psa_cache* c) {
+    int64_t total = 0;
+    for (int b = 0; b < c->desc.max_batch; ++b) total += visible_count(c, b);
+    const int64_t target_wgs = 4096;
+    int64_t per = (total * c->desc.n_kv_heads + target_wgs - 1) / target_wgs;
+    int64_t L = 256;
+    while (L < per && L < (int64_t)1 << 20) L += 256;
+    return (int)L;
+}
+
+bool valid_seq(const psa_cache* c, int32_t seq) { return seq >= 0 && seq < c->desc.max_batch; }
+
+}  // namespace
+
+PSA_API size_t psa_cache_bytes(const psa_cache_desc* desc) {
+    if (desc == nullptr) {
+        fail(PSA_ERR_ARG, "desc is NULL");
+        return 0;
+    }
+    psa::Layout L;
+    const char* why = nullptr;
+    if (!psa::compute_layout(*desc, &L, &why)) {
+        fail(PSA_ERR_ARG, why);
+        return 0;
+    }
+    return L.total;
+}
+
+PSA_API int psa_cache_layout(const psa_cache_desc* desc, psa_layout* out) {
+    if (desc == nullptr || out == nullptr) return fail(PSA_ERR_ARG, "NULL argument");
+    psa::Layout L;
+    const char* why = nullptr;
+    if (!psa::compute_layout(*desc, &L, &why)) return fail(PSA_ERR_ARG, why);
+    out->k_offset = L.k;
+    out->v_offset = L.v;
+    out->tags_offset = L.tags;
+    out->state_offset = L.state;
+    out->work_offset = L.inv_freq;
+    out->total_bytes = L.total;
+    out->slots = L.S;
+    out->elem_bytes = L.elem;
+    return PSA_OK;
+}
+
+PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t bytes,
+                             psa_stream stream, psa_cache** out) {
+    if (desc == nullptr || out == nullptr) return fail(PSA_ERR_ARG, "NULL argument");
+    psa::Layout L;
+    const char* why = nullptr;
+    if (!psa::compute_layout(*desc, &L, &why)) return fail(PSA_ERR_ARG, why);
+    if (dev_mem == nullptr) return fail(PSA_ERR_ARG, "dev_mem is NULL");
+    if (((uintptr_t)dev_mem & 255u) != 0) return fail(PSA_ERR_ARG, "dev_mem must be 256-byte aligned");
+    if (bytes < L.total)
+        return fail(PSA_ERR_ARG, "buffer too small: need " + std::to_string(L.total) + " bytes");
+
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+    psa_cache* c = new psa_cache();
+    c->desc = *desc;
+    c->L = L;
+    c->device = device;
+    c->cur = 0;
+    c->len.assign(desc->max_batch, 0);
+    c->pre.assign(desc->max_batch, -1);
+    c->split_tokens = 0;
+    c->profiling = false;
+    for (int i = 0; i < PSA_K_COUNT; ++i) {
+        c->total_ms[i] = 0.0;
+        c->launches[i] = 0;
+    }
+    char* base = (char*)dev_mem;
+    psa::DevCache& d = c->dev;
+    d.k = base + L.k;
+    d.v = base + L.v;
+    d.tags = (int32_t*)(base + L.tags);
+    int32_t* st = (int32_t*)(base + L.state);
+    d.len[0] = st;
+    d.len[1] = st + desc->max_batch;
+    d.pre = st + 2 * desc->max_batch;
+    d.nnew = st + 3 * desc->max_batch;
+    d.inv_freq = (double*)(base + L.inv_freq);
+    d.part_o = (float*)(base + L.part_o);
+    d.part_ml = (float*)(base + L.part_ml);
+    d.stage_k = base + L.stage_k;
+    d.B = desc->max_batch;
+    d.Hq = desc->n_q_heads;
+    d.Hkv = desc->n_kv_heads;
+    d.D = desc->head_dim;
+    d.Pmax = desc->prefix_max;
+    d.W = desc->window;
+    d.S = L.S;
+    d.dtype = desc->dtype;
+    d.max_chunk = desc->max_chunk;
+    d.max_splits = L.max_splits;
+    d.scale = desc->scale > 0.f ? desc->scale : (float)(1.0 / sqrt((double)desc->head_dim));
+
+    // theta_i = base^(-2i/D) in float64 on the host.
+    std::vector<double> theta(desc->head_dim / 2);
+    for (int i = 0; i < desc->head_dim / 2; ++i)
+        theta[i] = pow(desc->rope_base, (-2.0 * (double)i) / (double)desc->head_dim);
+    hipStream_t s = (hipStream_t)stream;
+    e = hipMemcpyAsync(d.inv_freq, theta.data(), theta.size() * sizeof(double),
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = psa::launch_init(d, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "cache initialisation");
+    }
+    *out = c;
+    return PSA_OK;
+}
+
+PSA_API int psa_cache_destroy(psa_cache* c) {
+    if (c == nullptr) return PSA_OK;
+    for (auto& ev : c->pending) {
+        hipEventDestroy(ev.start);
+        hipEventDestroy(ev.stop);
+    }
+    delete c;
+    return PSA_OK;
+}
+
+PSA_API int psa_seq_reset(psa_cache* c, int32_t seq, int32_t prefix_len, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    if (prefix_len < 0 || prefix_len > c->desc.prefix_max)
+        return fail(PSA_ERR_ARG, "prefix_len must be in [0, prefix_max]");
+    const hipError_t e = psa::launch_seq_reset(c->dev, seq, prefix_len, c->cur, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sequence reset");
+    c->len[seq] = 0;
+    c->pre[seq] = prefix_len;
+    return PSA_OK;
+}
+
+PSA_API int psa_append(psa_cache* c, const int32_t* n_new_host, int32_t n_uniform, const void* k,
+                       const void* v, int32_t n_stride, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (n_stride < 0) return fail(PSA_ERR_ARG, "n_stride must be >= 0");
+    const int B = c->desc.max_batch;
+    bool any = false;
+    for (int b = 0; b < B; ++b) {
+        const int32_t nb = n_new_host ? n_new_host[b] : n_uniform;
+        if (nb < 0 || nb > n_stride) return fail(PSA_ERR_ARG, "token count outside [0, n_stride]");
+        if (nb == 0) continue;
+        any = true;
+        if (c->pre[b] < 0) return fail(PSA_ERR_STATE, "append to a sequence that was never reset");
+        if (c->len[b] + nb > INT32_MAX) return fail(PSA_ERR_OVERFLOW, "sequence length overflow");
+    }
+    if (!any) return PSA_OK;
+    if (k == nullptr || v == nullptr) return fail(PSA_ERR_ARG, "k or v is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    if (n_new_host != nullptr) {
+        const hipError_t e = hipMemcpyAsync(c->dev.nnew, n_new_host, (size_t)B * sizeof(int32_t),
+                                            hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "token-count upload");
+    }
+    const int cur = c->cur;
+    const int rc = timed(c, PSA_K_APPEND, s, "append", [&] {
+        return psa::launch_append(c->dev, k, v, n_stride, n_uniform, n_new_host != nullptr, 0, cur, s);
+    });
+    if (rc != PSA_OK) return rc;
+    c->cur ^= 1;
+    for (int b = 0; b < B; ++b) c->len[b] += n_new_host ? n_new_host[b] : n_uniform;
+    return PSA_OK;
+}
+
+PSA_API int psa_decode_attn(psa_cache* c, const void* q, void* out, float* lse, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (q == nullptr || out == nullptr) return fail(PSA_ERR_ARG, "q or out is NULL");
+    const int B = c->desc.max_batch;
+    for (int b = 0; b < B; ++b) {
+        if (c->pre[b] < 0) return fail(PSA_ERR_STATE, "decode on a sequence that was never reset");
+        if (c->len[b] < 1) return fail(PSA_ERR_STATE, "decode on an empty sequence");
+    }
+    const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
+    int64_t max_ns = 1;
+    for (int b = 0; b < B; ++b) {
+        const int64_t ns = (visible_count(c, b) + L - 1) / L;
+        if (ns > max_ns) max_ns = ns;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int cur = c->cur;
+    int rc = timed(c, PSA_K_DECODE, s, "decode partial", [&] {
+        return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, s);
+    });
+    if (rc != PSA_OK) return rc;
+    return timed(c, PSA_K_MERGE, s, "split merge",
+                 [&] { return psa::launch_merge(c->dev, out, lse, L, cur, s); });
+}
+
+PSA_API int psa_prefill_attn(psa_cache* c, int32_t chunk, const void* q, const void* k,
+                             const void* v, void* out, float* lse, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (c->desc.max_chunk < 1) return fail(PSA_ERR_ARG, "cache was created with max_chunk = 0");
+    if (chunk < 1 || chunk > c->desc.max_chunk) return fail(PSA_ERR_ARG, "chunk must be in [1, max_chunk]");
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return fail(PSA_ERR_ARG, "q, k, v or out is NULL");
+    const int B = c->desc.max_batch;
+    for (int b = 0; b < B; ++b) {
+        if (c->pre[b] < 0) return fail(PSA_ERR_STATE, "prefill on a sequence that was never reset");
+        if (c->len[b] + chunk > INT32_MAX) return fail(PSA_ERR_OVERFLOW, "sequence length overflow");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int cur = c->cur;
+    int rc = timed(c, PSA_K_PREFILL_STAGE, s, "prefill stage",
+                   [&] { return psa::launch_prefill_stage(c->dev, k, chunk, cur, s); });
+    if (rc != PSA_OK) return rc;
+    rc = timed(c, PSA_K_PREFILL, s, "prefill attention",
+               [&] { return psa::launch_prefill(c->dev, q, v, out, lse, chunk, cur, s); });
+    if (rc != PSA_OK) return rc;
+    rc = timed(c, PSA_K_APPEND, s, "prefill commit", [&] {
+        return psa::launch_append(c->dev, c->dev.stage_k, v, chunk, chunk, 0, 1, cur, s);
+    });
+    if (rc != PSA_OK) return rc;
+    c->cur ^= 1;
+    for (int b = 0; b < B; ++b) c->len[b] += chunk;
+    return PSA_OK;
+}
+
+PSA_API int psa_export(psa_cache* c, int32_t seq, void* k_host, void* v_host, int32_t* pos_host,
+                       int32_t* count, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (count == nullptr) return fail(PSA_ERR_ARG, "count is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    if (c->pre[seq] < 0) return fail(PSA_ERR_STATE, "export of a sequence that was never reset");
+    const psa::DevCache& d = c->dev;
+    const int64_t n = c->len[seq], P = c->pre[seq], W = d.W;
+    const int64_t n_pre = n < P ? n : P;
+    const int64_t cnt = visible_count(c, seq);
+    const int64_t base = (n - W > P) ? n - W : P;   // oldest window position
+    const int64_t head = (base - P) % W;             // ring slot holding it
+    const size_t elem = (size_t)c->L.elem, D = (size_t)d.D, S = (size_t)d.S, Hkv = (size_t)d.Hkv;
+    const size_t row = D * elem;
+    const size_t seq_bytes = Hkv * S * row;
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<char> kbuf, vbuf;
+    std::vector<int32_t> tags(S);
+    hipError_t e = hipSuccess;
+    if (k_host) {
+        kbuf.resize(seq_bytes);
+        e = hipMemcpyAsync(kbuf.data(), (const char*)d.k + (size_t)seq * seq_bytes, seq_bytes,
+                           hipMemcpyDeviceToHost, s);
+    }
+    if (e == hipSuccess && v_host) {
+        vbuf.resize(seq_bytes);
+        e = hipMemcpyAsync(vbuf.data(), (const char*)d.v + (size_t)seq * seq_bytes, seq_bytes,
+                           hipMemcpyDeviceToHost, s);
+    }
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(tags.data(), d.tags + (size_t)seq * S, S * sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "export copy");
+    // Logical order: prefix slots, then the ring from the oldest entry ([KV-Lean] 3.4).
+    for (int64_t i = 0; i < cnt; ++i) {
+        const size_t slot = i < n_pre ? (size_t)i : (size_t)(d.Pmax + (head + (i - n_pre)) % W);
+        if (pos_host) pos_host[i] = tags[slot];
+        for (size_t h = 0; h < Hkv; ++h) {
+            const size_t from = (h * S + slot) * row, to = ((size_t)i * Hkv + h) * row;
+            if (k_host) memcpy((char*)k_host + to, kbuf.data() + from, row);
+            if (v_host) memcpy((char*)v_host + to, vbuf.data() + from, row);
+        }
+    }
+    *count = (int32_t)cnt;
+    return PSA_OK;
+}
+
+PSA_API int64_t psa_seq_length(const psa_cache* c, int32_t seq) {
+    if (c == nullptr || !valid_seq(c, seq) || c->pre[seq] < 0) return -1;
+    return c->len[seq];
+}
+
+PSA_API int psa_set_split_tokens(psa_cache* c, int32_t tokens) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (tokens < 0 || tokens % psa::kSplitGranule != 0)
+        return fail(PSA_ERR_ARG, "split tokens must be 0 or a positive multiple of 128");
+    c->split_tokens = tokens;
+    return PSA_OK;
+}
+
+PSA_API int psa_profile(psa_cache* c, int32_t enable) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    for (auto& ev : c->pending) {
+        hipEventSynchronize(ev.stop);
+        hipEventDestroy(ev.start);
+        hipEventDestroy(ev.stop);
+    }
+    c->pending.clear();
+    if (enable) {
+        for (int i = 0; i < PSA_K_COUNT; ++i) {
+            c->total_ms[i] = 0.0;
+            c->launches[i] = 0;
+        }
+    }
+    c->profiling = enable != 0;
+    return PSA_OK;
+}
+
+PSA_API int psa_profile_read(psa_cache* c, int32_t kernel, double* total_ms, int64_t* launches) {
+    if (c == nullptr || total_ms == nullptr || launches == nullptr)
+        return fail(PSA_ERR_ARG, "NULL argument");
+    if (kernel < 0 || kernel >= PSA_K_COUNT) return fail(PSA_ERR_ARG, "unknown kernel id");
+    for (auto& ev : c->pending) {
+        hipError_t e = hipEventSynchronize(ev.stop);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.start, ev.stop);
+        hipEventDestroy(ev.start);
+        hipEventDestroy(ev.stop);
+        if (e != hipSuccess) {
+            c->pending.clear();
+            return hip_fail(e, "profiling event");
+        }
+        c->total_ms[ev.kernel] += ms;
+        c->launches[ev.kernel] += 1;
+    }
+    c->pending.clear();
+    *total_ms = c->total_ms[kernel];
+    *launches = c->launches[kernel];
+    return PSA_OK;
+}
+
+PSA_API const char* psa_status_string(int status) {
+    switch (status) {
+        case PSA_OK: return "ok";
+        case PSA_ERR_ARG: return "invalid argument";
+        case PSA_ERR_STATE: return "invalid state";
+        case PSA_ERR_OVERFLOW: return "sequence length overflow";
+        case PSA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+PSA_API const char* psa_last_error(void) { return g_err.c_str(); }

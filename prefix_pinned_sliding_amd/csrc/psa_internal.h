@@ -1,0 +1,54 @@
+// Internal declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/psa.h"
+
+namespace psa {
+
+constexpr int kSplitGranule = 128;   // decode split lengths are multiples of this
+constexpr int kMaxGroup = 8;         // largest supported H_q / H_kv
+
+// Device view of one cache: base pointers carved out of the caller's buffer.
+struct DevCache {
+    void* k;             // [B][Hkv][S][D] storage dtype
+    void* v;             // [B][Hkv][S][D]
+    int32_t* tags;       // [B][S]
+    int32_t* len[2];     // [B] history lengths; len[cur] is current, the other is written by append
+    int32_t* pre;        // [B] prefix length P_b
+    int32_t* nnew;       // [B] per-call token counts (ragged append)
+    double* inv_freq;    // [D/2] theta_i
+    float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
+    float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
+    void* stage_k;       // [B][Hkv][max_chunk][D] rotated prefill-chunk keys
+    int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits;
+    float scale;
+};
+
+struct Layout {
+    size_t k, v, tags, state, inv_freq, part_o, part_ml, stage_k, total;
+    int32_t S, elem, max_splits;
+};
+
+bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why);
+
+// Kernel launchers (stream-ordered, asynchronous). They return the launch status.
+hipError_t launch_init(const DevCache& c, hipStream_t s);
+hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int cur, hipStream_t s);
+// Append n tokens per sequence (n_uniform, or nnew[] on device when ragged != 0).
+// k/v: [B][n_stride][Hkv][D]; k_rotated != 0 means k already holds rotated, rounded keys.
+hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_stride,
+                         int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s);
+hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
+                                 int grid_splits, int cur, hipStream_t s);
+hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,
+                        hipStream_t s);
+hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur,
+                                hipStream_t s);
+hipError_t launch_prefill(const DevCache& c, const void* q, const void* v, void* out, float* lse,
+                          int chunk, int cur, hipStream_t s);
+
+}  // namespace psa

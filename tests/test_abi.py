@@ -1,0 +1,119 @@
+"""The C-ABI library loads without a GPU, exports every function include/psa.h declares,
+and rejects invalid arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def psa():
+    import prefix_pinned_sliding_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["psa_cache_bytes", "psa_cache_create", "psa_cache_destroy", "psa_seq_reset",
+                 "psa_append", "psa_decode_attn", "psa_prefill_attn", "psa_export",
+                 "psa_seq_length", "psa_status_string", "psa_last_error"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(psa):
+    raw = ctypes.CDLL(psa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_exports_only_the_c_abi(psa):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", psa.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {s for s in syms if s.startswith("psa_")} == set(declared_functions())
+
+
+def good_desc(psa, **kw):
+    d = dict(max_batch=4, n_q_heads=16, n_kv_heads=8, head_dim=128, prefix_max=100, window=4096,
+             max_chunk=512)
+    d.update(kw)
+    return psa.make_desc(**d)
+
+
+def test_cache_bytes_and_layout(psa):
+    d = good_desc(psa)
+    n = psa.cache_bytes(d)
+    L = psa.cache_layout(d)
+    assert L.total_bytes == n
+    S = 100 + 4096
+    assert L.slots == S and L.elem_bytes == 2
+    kv = 4 * 8 * S * 128 * 2
+    assert L.v_offset >= L.k_offset + kv and L.tags_offset >= L.v_offset + kv
+    for off in (L.k_offset, L.v_offset, L.tags_offset, L.state_offset, L.work_offset):
+        assert off % 256 == 0
+    assert n >= 2 * kv + 4 * S * 4
+
+
+@pytest.mark.parametrize("bad", [
+    dict(max_batch=0), dict(n_kv_heads=0), dict(n_q_heads=12), dict(n_q_heads=48, n_kv_heads=4),
+    dict(head_dim=96), dict(prefix_max=-1), dict(window=0), dict(max_chunk=-1),
+])
+def test_invalid_descriptions_are_rejected(psa, bad):
+    d = good_desc(psa, **bad)
+    assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0
+    out = psa.Layout()
+    assert psa.lib.psa_cache_layout(ctypes.byref(d), ctypes.byref(out)) == psa.PSA_ERR_ARG
+    assert psa.lib.psa_last_error().decode() != ""
+
+
+def test_invalid_rope_base_scale_dtype(psa):
+    for field, val in [("rope_base", 0.0), ("rope_base", float("inf")), ("scale", -1.0),
+                       ("dtype", 7), ("reserved", 1)]:
+        d = good_desc(psa)
+        setattr(d, field, val)
+        assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0, field
+
+
+def test_create_rejects_bad_buffers_before_any_device_call(psa):
+    d = good_desc(psa)
+    n = psa.cache_bytes(d)
+    h = ctypes.c_void_p()
+    lib = psa.lib
+    assert lib.psa_cache_create(ctypes.byref(d), None, n, None, ctypes.byref(h)) == psa.PSA_ERR_ARG
+    assert lib.psa_cache_create(ctypes.byref(d), ctypes.c_void_p(0x1000 + 8), n, None,
+                                ctypes.byref(h)) == psa.PSA_ERR_ARG
+    assert "aligned" in lib.psa_last_error().decode()
+    assert lib.psa_cache_create(ctypes.byref(d), ctypes.c_void_p(0x100000), n - 1, None,
+                                ctypes.byref(h)) == psa.PSA_ERR_ARG
+    assert "too small" in lib.psa_last_error().decode()
+    assert h.value is None
+
+
+def test_null_handle_calls(psa):
+    lib = psa.lib
+    assert lib.psa_cache_destroy(None) == psa.PSA_OK
+    assert lib.psa_seq_reset(None, 0, 0, None) == psa.PSA_ERR_ARG
+    assert lib.psa_append(None, None, 1, None, None, 1, None) == psa.PSA_ERR_ARG
+    assert lib.psa_decode_attn(None, None, None, None, None) == psa.PSA_ERR_ARG
+    assert lib.psa_prefill_attn(None, 1, None, None, None, None, None, None) == psa.PSA_ERR_ARG
+    cnt = ctypes.c_int32()
+    assert lib.psa_export(None, 0, None, None, None, ctypes.byref(cnt), None) == psa.PSA_ERR_ARG
+    assert lib.psa_seq_length(None, 0) == -1
+    assert lib.psa_set_split_tokens(None, 0) == psa.PSA_ERR_ARG
+
+
+def test_status_strings(psa):
+    for s in range(5):
+        assert psa.lib.psa_status_string(s).decode()
+    assert psa.lib.psa_status_string(99).decode() == "unknown status"

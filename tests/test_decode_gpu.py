@@ -1,0 +1,155 @@
+"""Decode attention on the GPU against the float64 oracle (masked full history).
+
+Tolerances: max|out - ref| <= 1e-5 for float32; for bfloat16, max-abs <= 2e-2 and
+||out - ref||_2 / ||ref||_2 <= 5e-3 over each call's checked outputs. lse (float32)
+within 1e-4 absolute. Full-size workloads are checked on sampled sequences (all heads)
+that the oracle computes one by one; every output is checked to be finite."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn
+from synth import configs, drive
+
+pytestmark = pytest.mark.gpu
+
+
+def tol_check(out: np.ndarray, ref: np.ndarray, dtype, what=""):
+    err = np.abs(out - ref).max()
+    if dtype == torch.float32:
+        assert err <= 1e-5, f"{what} max-abs {err}"
+    else:
+        rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+        assert err <= 2e-2 and rel <= 5e-3, f"{what} max-abs {err} rel-l2 {rel}"
+    return err
+
+
+def oracle_decode(wl, b, p, q_row):
+    return attn.decode_query(q_row, p, drive.hist_provider(wl, b), wl.prefix[b], wl.window,
+                             wl.n_kv_heads, wl.rope_base, wl.scale)
+
+
+def step_and_check(c, wl, n_before, seqs=None, lse=True):
+    """Append the token at p = n_before[b], decode it, compare chosen sequences."""
+    B = wl.batch
+    k, v = drive.kv_block(wl, n_before, 1, "cuda")
+    c.append(k, v)
+    q = drive.queries(wl, n_before, "cuda")
+    lse_t = torch.empty((B, wl.n_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    out = c.decode(q, lse=lse_t)
+    torch.cuda.synchronize()
+    o = out.double().cpu().numpy()
+    assert np.isfinite(o).all()
+    qc = q.double().cpu().numpy()
+    seqs = range(B) if seqs is None else seqs
+    outs, refs = [], []
+    for b in seqs:
+        ref, ref_lse = oracle_decode(wl, b, n_before[b], qc[b])
+        outs.append(o[b])
+        refs.append(ref)
+        if lse:
+            np.testing.assert_allclose(lse_t[b].cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
+    return np.stack(outs), np.stack(refs)
+
+
+def test_tiny_fp32_all_steps():
+    wl = configs.tiny_fp32()
+    c = drive.make_cache(wl)
+    c.reset(0, wl.prefix[0])
+    worst = 0.0
+    for p in range(wl.steps):
+        o, r = step_and_check(c, wl, [p])
+        worst = max(worst, tol_check(o, r, wl.dtype, f"step {p}"))
+    print(f"tiny fp32: 200 steps, worst max-abs {worst:.2e}")
+
+
+def test_first_token_returns_its_value():
+    wl = configs.Workload("first", torch.bfloat16, 2, 8, 4, 128, 8, [3, 0], [1, 1], "decode")
+    c = drive.make_cache(wl)
+    for b in range(2):
+        c.reset(b, wl.prefix[b])
+    k, v = drive.kv_block(wl, [0, 0], 1, "cuda")
+    c.append(k, v)
+    out = c.decode(drive.queries(wl, [0, 0], "cuda"))
+    G = 2
+    want = v[:, 0].repeat_interleave(G, dim=1)
+    assert torch.equal(out, want)
+
+
+GRID = [(torch.bfloat16, 128, 16, 8), (torch.bfloat16, 128, 32, 8), (torch.bfloat16, 64, 8, 8),
+        (torch.bfloat16, 128, 64, 8), (torch.float32, 64, 8, 4), (torch.float32, 128, 16, 8),
+        (torch.bfloat16, 64, 32, 4)]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", GRID)
+def test_phases_and_shapes(dtype, D, Hq, Hkv):
+    # Sequences in every phase: inside the prefix, window filling, exactly full, first
+    # eviction, long after; plus P = 0 (plain sliding window).
+    W = 37
+    prefix = [7, 3, 20, 0, 5, 12]
+    n_hist = [3, 15, 20 + W - 1, 40, 5 + W, 900]
+    wl = configs.Workload("grid", dtype, len(prefix), Hq, Hkv, D, W, prefix, [1] * 6, "decode")
+    c = drive.make_cache(wl)
+    drive.fill(c, wl, n_hist)
+    o, r = step_and_check(c, wl, n_hist)
+    tol_check(o, r, dtype)
+
+
+def test_split_count_invariance():
+    W = 1000
+    prefix = [100, 0, 37, 200]
+    n_hist = [5000, 1200, 700, 250]
+    wl = configs.Workload("splits", torch.bfloat16, 4, 16, 8, 128, W, prefix, [1] * 4, "decode")
+    c = drive.make_cache(wl)
+    drive.fill(c, wl, n_hist)
+    k, v = drive.kv_block(wl, n_hist, 1, "cuda")
+    c.append(k, v)
+    q = drive.queries(wl, n_hist, "cuda")
+    qc = q.double().cpu().numpy()
+    refs = [oracle_decode(wl, b, n_hist[b], qc[b]) for b in range(4)]
+    lses = []
+    for tokens in (128, 256, 384, 1152, 0):
+        c.set_split_tokens(tokens)
+        lse = torch.empty((4, 16), dtype=torch.float32, device="cuda")
+        out = c.decode(q, lse=lse).double().cpu().numpy()
+        for b in range(4):
+            tol_check(out[b], refs[b][0], wl.dtype, f"split {tokens} seq {b}")
+        lses.append(lse.cpu().numpy())
+    for x in lses[1:]:
+        np.testing.assert_allclose(x, lses[0], rtol=0, atol=2e-5)
+
+
+def run_full(wl, seqs):
+    n_hist = [t - 1 for t in wl.start]
+    c = drive.make_cache(wl)
+    drive.fill(c, wl, n_hist)
+    o, r = step_and_check(c, wl, n_hist, seqs=seqs)
+    err = tol_check(o, r, wl.dtype, wl.name)
+    print(f"{wl.name}: sampled {len(seqs)} sequences, max-abs {err:.2e}")
+
+
+def test_decode_p100_w4096_full_size():
+    run_full(configs.decode_p100_w4096(), [0, 17, 42, 63])
+
+
+def test_decode_p512_w16384_full_size():
+    run_full(configs.decode_p512_w16384(), [0, 13, 31])
+
+
+def test_ragged_decode_64_steps():
+    wl = configs.ragged_decode()
+    B = wl.batch
+    n = [t - 1 for t in wl.start]
+    # sampled: shortest start relative to its prefix (inside or near the prefix), a window
+    # still filling, just past full, and the longest histories
+    order = sorted(range(B), key=lambda b: n[b] - wl.prefix[b])
+    seqs = sorted(set([order[0], order[1], order[B // 8], order[B // 3], order[-1], order[-2]]))
+    c = drive.make_cache(wl)
+    drive.fill(c, wl, n)
+    worst = 0.0
+    for step in range(wl.steps):
+        check = seqs if step in (0, 1, 31, 63) else seqs[:2]
+        o, r = step_and_check(c, wl, n, seqs=check, lse=step in (0, 63))
+        worst = max(worst, tol_check(o, r, wl.dtype, f"step {step}"))
+        n = [x + 1 for x in n]
+    print(f"ragged: 64 steps, worst max-abs {worst:.2e}")
