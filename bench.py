@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-calls", type=int, default=10)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB with torch (counter calibration)")
     return ap.parse_args()
@@ -102,11 +104,78 @@ def cpu_baseline(wl, n_now, q_rows, budget_s: float):
                       f"query heads, float64 NumPy, 1 thread), {elapsed:.1f} s"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(calls: int, warmup: int = 2):
+    """Chunked prefill: 8 sequences each take a 512-token chunk at t ~ U{8192..65536}.
+
+    Each call attends the chunk (staging, MFMA attention) and appends it; the state
+    advances by 512 tokens per call. Algorithmic work per call: 4 * H_q * D * sum over
+    the chunk's queries of |A(p)| flops (QK^T and PV over the visible set).
+    """
+    import torch
+
+    import prefix_pinned_sliding_amd as psa
+    from synth import configs, drive
+
+    wl = configs.prefill_chunk512()
+    C = wl.chunk
+    n0 = [t - 1 for t in wl.start]
+    c = drive.make_cache(wl, max_chunk=C)
+    drive.fill(c, wl, n0)
+    total = warmup + 2 * calls
+    inputs = []
+    for i in range(total):
+        starts = [n + i * C for n in n0]
+        q = drive.query_block(wl, starts, C, "cuda")
+        k, v = drive.kv_block(wl, starts, C, "cuda")
+        inputs.append((q, k, v))
+    out = torch.empty_like(inputs[0][0])
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        c.prefill(*inputs[i], out=out)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(warmup, warmup + calls):
+        c.prefill(*inputs[i], out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_call = start.elapsed_time(stop) / calls
+    c.profile(True)
+    for i in range(warmup + calls, total):
+        c.prefill(*inputs[i], out=out)
+    torch.cuda.synchronize()
+    times = {name: c.profile_read(k) for k, name in psa.KERNEL_NAMES.items()}
+    c.profile(False)
+    pf_ms, pf_n = times["prefill"]
+    pf_avg_s = pf_ms / pf_n / 1e3
+
+    def visible(p, P):
+        return min(p + 1, P + wl.window)
+
+    flops = 0.0
+    for i in range(warmup + calls, total):
+        for b in range(wl.batch):
+            base = n0[b] + i * C
+            flops += sum(visible(base + j, wl.prefix[b]) for j in range(C))
+    flops = flops / calls * 4 * wl.n_q_heads * wl.head_dim
+    tflops = flops / pf_avg_s / 1e12
+    return {"workload": wl.name, "calls": calls, "ms_per_call": ms_call,
+            "tokens_per_s": wl.batch * C / (ms_call / 1e3),
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "kernel": "prefill", "kernel_avg_us": pf_avg_s * 1e6,
+                         "flops_per_launch": flops},
+            "kernels_avg_us": {k: (ms / n * 1e3 if n else None) for k, (ms, n) in times.items()}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence and by KV head with no exchange, see the design notes)",
+              "(run one process per GPU; sequences and KV heads shard with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -204,6 +273,12 @@ def main():
                      "kernel_avg_us": dec_avg_s * 1e6, "bytes_per_launch": launch_bytes},
         "kernels_avg_us": {k: (ms / n * 1e3 if n else None) for k, (ms, n) in times.items()},
     }
+
+    if not args.no_prefill and args.workload == "decode_p100_w4096":
+        del c
+        torch.cuda.empty_cache()
+        print("[bench] chunked prefill", file=sys.stderr, flush=True)
+        result["prefill"] = bench_prefill(args.prefill_calls)
 
     if not args.no_cpu_baseline:
         qc = qs[total - 1].double().cpu().numpy()

@@ -1,5 +1,5 @@
-// Ring append with rotary encoding at the absolute position (K1), the fills used by
-// cache creation and sequence reset, and the staging rotation of a prefill chunk.
+// Ring append with rotary encoding at the absolute position (K1) and the fills used by
+// cache creation and sequence reset.
 //
 // [PS] 03 generation loop: the prefix KV is kept for good, each new token joins the
 // window, and the window drops its oldest token once it holds more than W.
@@ -7,6 +7,7 @@
 // absolute position, and reused unchanged while it stays cached.
 // [KV-Lean] 3.2: every slot carries the absolute position of the token it holds.
 #include "psa_internal.h"
+#include "rope_round.h"
 
 namespace psa {
 namespace {
@@ -18,58 +19,11 @@ template <int DT> struct Elem;
 template <> struct Elem<PSA_BF16> { using T = uint16_t; };
 template <> struct Elem<PSA_F32> { using T = float; };
 
-__device__ __forceinline__ double to_f64(uint16_t b) {
-    return (double)__uint_as_float((uint32_t)b << 16);
-}
+__device__ __forceinline__ double to_f64(uint16_t b) { return bf16_bits_to_f64(b); }
 __device__ __forceinline__ double to_f64(float f) { return (double)f; }
 
-// float64 -> bfloat16 bits, one rounding to nearest, ties to even, on the float64 bit
-// fields: results below 2^-126 become bfloat16 subnormals, a carry out of the
-// fraction bumps the exponent, overflow gives infinity, NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-    const uint64_t u = (uint64_t)__double_as_longlong(x);
-    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
-    const int e = (int)((u >> 52) & 0x7FF);
-    const uint64_t frac = u & ((1ull << 52) - 1);
-    if (e == 0x7FF) return sign | (frac ? 0x7FC0 : 0x7F80);
-    if (e == 0) return sign;                       // float64 zero or subnormal
-    const int E = e - 1023;
-    if (E >= -126) {
-        uint64_t body = ((uint64_t)(E + 127) << 7) | (frac >> 45);
-        const uint64_t rem = frac & ((1ull << 45) - 1);
-        const uint64_t half = 1ull << 44;
-        if (rem > half || (rem == half && (body & 1ull))) ++body;
-        if (body >= 0x7F80ull) body = 0x7F80ull;
-        return sign | (uint16_t)body;
-    }
-    const int sh = -E - 81;                        // leaves units of 2^-133
-    if (sh >= 64) return sign;
-    const uint64_t full = frac | (1ull << 52);
-    uint64_t kept = full >> sh;
-    const uint64_t rem = full & ((1ull << sh) - 1);
-    const uint64_t half = 1ull << (sh - 1);
-    if (rem > half || (rem == half && (kept & 1ull))) ++kept;
-    return sign | (uint16_t)kept;
-}
-
-__device__ __forceinline__ uint16_t store_as(double x, uint16_t*) { return f64_to_bf16(x); }
+__device__ __forceinline__ uint16_t store_as(double x, uint16_t*) { return f64_to_bf16_bits(x); }
 __device__ __forceinline__ float store_as(double x, float*) { return (float)x; }
-
-// Rotate the pair (x, y) by the angle p * theta in float64: (x c - y s, x s + y c), each
-// product and sum rounded on its own.
-__device__ __forceinline__ void rotate_pair(double x, double y, int p, double theta, double* xr,
-                                            double* yr) {
-#pragma clang fp contract(off)
-    const double phi = (double)p * theta;
-    double sn, cs;
-    sincos(phi, &sn, &cs);
-    const double a = x * cs;
-    const double b = y * sn;
-    const double c = x * sn;
-    const double d = y * cs;
-    *xr = a - b;
-    *yr = c + d;
-}
 
 __global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_state) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -141,32 +95,6 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
     if (h == 0 && i == 0) c.tags[(size_t)b * c.S + slot] = p;
 }
 
-// Rotate a prefill chunk's keys into the staging buffer: stage[b][j][h][:] holds
-// RNE(rotate(k[b][j][h][:], len[b] + j)), the exact bytes the append will store.
-template <int DT, int D>
-__global__ __launch_bounds__(kBlock) void stage_kernel(DevCache c, const typename Elem<DT>::T* k,
-                                                       int chunk,
-                                                       const int32_t* __restrict__ len_cur) {
-    using T = typename Elem<DT>::T;
-    constexpr int H = D / 2;
-    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    const size_t total = (size_t)c.B * chunk * c.Hkv * H;
-    if (idx >= total) return;
-    const int i = (int)(idx % H);
-    size_t r = idx / H;
-    const int h = (int)(r % c.Hkv);
-    r /= c.Hkv;
-    const int j = (int)(r % chunk);
-    const int b = (int)(r / chunk);
-    const int p = len_cur[b] + j;
-    const size_t off = (((size_t)b * chunk + j) * c.Hkv + h) * D;
-    double xr, yr;
-    rotate_pair(to_f64(k[off + i]), to_f64(k[off + i + H]), p, c.inv_freq[i], &xr, &yr);
-    T* out = (T*)c.stage_k;
-    out[off + i] = store_as(xr, (T*)nullptr);
-    out[off + i + H] = store_as(yr, (T*)nullptr);
-}
-
 inline unsigned blocks_for(size_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
 
 }  // namespace
@@ -200,22 +128,6 @@ hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_
         if (c.D == 128) PSA_APPEND(PSA_F32, 128); else PSA_APPEND(PSA_F32, 64);
     }
 #undef PSA_APPEND
-    return hipGetLastError();
-}
-
-hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur,
-                                hipStream_t s) {
-    const size_t total = (size_t)c.B * chunk * c.Hkv * (c.D / 2);
-    const dim3 grid(blocks_for(total));
-#define PSA_STAGE(DT, DD)                                                                       \
-    hipLaunchKernelGGL((stage_kernel<DT, DD>), grid, dim3(kBlock), 0, s, c,                     \
-                       (const typename Elem<DT>::T*)k, chunk, c.len[cur])
-    if (c.dtype == PSA_BF16) {
-        if (c.D == 128) PSA_STAGE(PSA_BF16, 128); else PSA_STAGE(PSA_BF16, 64);
-    } else {
-        if (c.D == 128) PSA_STAGE(PSA_F32, 128); else PSA_STAGE(PSA_F32, 64);
-    }
-#undef PSA_STAGE
     return hipGetLastError();
 }
 

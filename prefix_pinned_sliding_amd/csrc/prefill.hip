@@ -1,11 +1,385 @@
-// Chunked-prefill attention on MFMA (K4). Not built yet: the launcher reports an error.
+// Chunked-prefill attention on MFMA (K4) and the staging of a chunk's rotated queries and
+// keys.
+//
+// A chunk of C new tokens at positions n .. n + C - 1 of a sequence: query row c (at
+// p = n + c) attends to A(p) ([PS] 03): the pinned prefix, the window [p - W + 1, p] and
+// so the chunk's own tokens up to p. Keys come from three ranges, walked in tiles of
+// BN = 64 positions:
+//   prefix   positions [0, min(n, P)) in the cache's prefix slots,
+//   old ring positions [max(P, p_lo - W + 1), n) in the ring (slot (j - P) mod W),
+//   chunk    positions [n, p_hi] from the staged rotated keys and the input values,
+// where [p_lo, p_hi] are the positions of the workgroup's rows. A tile is skipped when no
+// row sees any of its keys, computed without masks when every row sees every key, and
+// masked element by element otherwise ([PS] 06: whole tiles in the evicted middle are never
+// loaded, partially covered tiles are masked).
+//
+// Per workgroup: 4 waves, 128 rows = (128 / G) positions x G query heads of one KV head, so
+// every K/V tile in LDS serves all G heads. Each wave owns 32 rows (two 16-row blocks).
+// Both products run on v_mfma_f32_16x16x32_bf16 in transposed form: S^T = K Q^T (K from
+// LDS as the A operand, Q^T held in registers as B) and O^T = V^T P^T (V^T from LDS, P^T
+// from registers). In S^T's accumulator layout each lane holds one row (query) and four
+// keys, which is exactly the B-operand layout P^T needs, so probabilities never leave
+// registers; row maxima need one cross-lane exchange per tile, row sums are reduced once
+// at the end. V is transposed into LDS while staging. Softmax runs on exp2 with the scale
+// folded into the staged queries; the running max is raised only when a tile exceeds it
+// by more than 2^8.
 #include "psa_internal.h"
+#include "rope_round.h"
 
 namespace psa {
+namespace {
 
-hipError_t launch_prefill(const DevCache&, const void*, const void*, void*, float*, int, int,
-                          hipStream_t) {
-    return hipErrorNotSupported;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kBlock = 64 * kWaves;
+constexpr int kRows = 128;              // rows (position x head) per workgroup
+constexpr int kBN = 64;                 // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNeg = -1.0e30f;        // logit of a masked pair (finite: no inf - inf)
+constexpr float kRescaleSlack = 8.0f;
+
+// float64 -> bfloat16 for staged queries: the same single rounding as stored keys.
+__device__ __forceinline__ uint16_t q_to_bf16(double x) { return f64_to_bf16_bits(x); }
+
+// Stage a chunk: keys rotated at their absolute positions and rounded once (the bytes the
+// cache will hold), queries rotated, multiplied by scale * log2(e) and rounded to bf16.
+// One thread per (sequence, token, head, pair); heads [0, Hkv) are keys, the rest queries.
+template <int D>
+__global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const uint16_t* q,
+                                                             const uint16_t* k, int chunk,
+                                                             const int32_t* __restrict__ len_cur) {
+    constexpr int H = D / 2;
+    const int heads = c.Hkv + c.Hq;
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t total = (size_t)c.B * chunk * heads * H;
+    if (idx >= total) return;
+    const int i = (int)(idx % H);
+    size_t r = idx / H;
+    const int hh = (int)(r % heads);
+    r /= heads;
+    const int j = (int)(r % chunk);
+    const int b = (int)(r / chunk);
+    const int p = len_cur[b] + j;
+    const bool is_key = hh < c.Hkv;
+    const size_t off = is_key ? (((size_t)b * chunk + j) * c.Hkv + hh) * D
+                              : (((size_t)b * chunk + j) * c.Hq + (hh - c.Hkv)) * D;
+    const uint16_t* src = is_key ? k : q;
+    double xr, yr;
+    rotate_pair(bf16_bits_to_f64(src[off + i]), bf16_bits_to_f64(src[off + i + H]), p,
+                c.inv_freq[i], &xr, &yr);
+    if (is_key) {
+        uint16_t* out = (uint16_t*)c.stage_k;
+        out[off + i] = f64_to_bf16_bits(xr);
+        out[off + i + H] = f64_to_bf16_bits(yr);
+    } else {
+        const double sc = (double)c.scale * (double)kLog2e;
+        uint16_t* out = (uint16_t*)c.stage_q;
+        out[off + i] = q_to_bf16(xr * sc);
+        out[off + i + H] = q_to_bf16(yr * sc);
+    }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// Max over lanes l, l^16, l^32, l^48 (the four lane groups holding one row).
+__device__ __forceinline__ float row_max4(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float row_sum4(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
+                                                            uint16_t* __restrict__ out,
+                                                            float* __restrict__ lse, int chunk,
+                                                            int n_qtiles,
+                                                            const int32_t* __restrict__ len_cur) {
+    constexpr int BQ = kRows / G;         // positions per workgroup
+    constexpr int KS = D / 32;            // k-steps of S^T = K Q^T
+    constexpr int DB = D / 16;            // d-blocks of O^T
+    constexpr int KB = kBN / 16;          // key blocks per tile
+    constexpr int PVS = kBN / 32;         // k-steps of O^T = V^T P^T
+    constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
+    constexpr int VSTR = kBN + 4;         // LDS row stride of V^T (elements)
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
+
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
+
+    // XCD-aware tile order: workgroup L runs on XCD L % 8; give each XCD a contiguous run
+    // of logical tiles so all query tiles of one (sequence, KV head) share that XCD's L2.
+    const int total = n_qtiles * c.Hkv * c.B;
+    const int per_xcd = (total + 7) / 8;
+    const int L = blockIdx.x;
+    const int logical = (L % 8) * per_xcd + L / 8;
+    if (logical >= total) return;
+    const int qt = logical % n_qtiles;
+    const int bh = logical / n_qtiles;
+    const int h = bh % c.Hkv;
+    const int b = bh / c.Hkv;
+
+    const int n = len_cur[b];
+    const int P = c.pre[b];
+    const int W = c.W;
+    const int c0 = qt * BQ;
+    const int p_lo = n + c0;
+    const int p_hi = n + min(c0 + BQ, chunk) - 1;   // last valid row position
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    // rows of this lane: r = 32 * wave + 16 * rb + l16, position p = n + c0 + r / G
+    int row_pos[2];
+    bf16x8 qop[2][KS];
+    const uint16_t* stage_q = (const uint16_t*)c.stage_q;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = 32 * wave + 16 * rb + l16;
+        const int cl = min(c0 + r / G, chunk - 1);
+        const int g = r % G;
+        row_pos[rb] = n + c0 + r / G;
+        const uint16_t* qrow = stage_q + (((size_t)b * chunk + cl) * c.Hq + h * G + g) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32 + 8 * lg));
+    }
+
+    f32x4 o[2][DB];
+    float m[2], lp[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        m[rb] = kNeg;
+        lp[rb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
+    const uint16_t* Kc = (const uint16_t*)c.k + head_off;
+    const uint16_t* Vc = (const uint16_t*)c.v + head_off;
+    const uint16_t* Ks = (const uint16_t*)c.stage_k;
+
+    // segment bounds in position space
+    const int nA = min(n, P);
+    const int jB0 = max(P, p_lo - W + 1);
+    const int seg_lo[3] = {0, n > P ? jB0 : n, n};
+    const int seg_hi[3] = {nA, n, p_hi + 1};
+
+#pragma unroll 1
+    for (int seg = 0; seg < 3; ++seg) {
+#pragma unroll 1
+        for (int t0 = seg_lo[seg]; t0 < seg_hi[seg]; t0 += kBN) {
+            const int t1 = min(t0 + kBN, seg_hi[seg]);
+            // no row sees any key of the tile: all keys past the prefix and older than the
+            // window of the first row
+            if (t0 >= P && t1 - 1 < p_lo - W + 1) continue;
+            const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) &&
+                              (t1 - 1 < P || t0 >= p_hi - W + 1);
+
+            // ---- stage the tile: K rows as is, V transposed -----------------------------
+            __syncthreads();
+#pragma unroll
+            for (int rr = 0; rr < (kBN * CPR) / kBlock; ++rr) {
+                const int ci = tid + kBlock * rr;
+                const int kk = ci / CPR, col = ci % CPR;
+                const int j = min(t0 + kk, t1 - 1);
+                const uint16_t* src;
+                if (seg == 0) src = Kc + (size_t)j * D;
+                else if (seg == 1) src = Kc + (size_t)(c.Pmax + (j - P) % W) * D;
+                else src = Ks + (((size_t)b * chunk + (j - n)) * c.Hkv + h) * D;
+                *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) =
+                    *reinterpret_cast<const u32x4*>(src + col * 8);
+            }
+            {
+                const int dc = tid % CPR, kq = tid / CPR;
+                if (kq < kBN / 4) {
+                    u32x4 w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = min(t0 + 4 * kq + e, t1 - 1);
+                        const uint16_t* src;
+                        if (seg == 0) src = Vc + (size_t)j * D;
+                        else if (seg == 1) src = Vc + (size_t)(c.Pmax + (j - P) % W) * D;
+                        else src = v_in + (((size_t)b * chunk + (j - n)) * c.Hkv + h) * D;
+                        w[e] = *reinterpret_cast<const u32x4*>(src + dc * 8);
+                    }
+                    // 4 keys x 8 dims -> 8 rows of V^T with 4 consecutive keys each
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const uint32_t a0 = w[0][x], a1 = w[1][x], a2 = w[2][x], a3 = w[3][x];
+                        u32x2 lo, hi;   // dims 2x (low halves) and 2x + 1 (high halves)
+                        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+                        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+                        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+                        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+                        const int d0 = dc * 8 + 2 * x;
+                        *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + 4 * kq) = lo;
+                        *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + 4 * kq) = hi;
+                    }
+                }
+            }
+            __syncthreads();
+
+            // ---- S^T = K Q^T ------------------------------------------------------------
+            f32x4 s[2][KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = as_bf16x8(
+                        *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
+                    s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0][ks], s[0][kb], 0, 0, 0);
+                    s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1][ks], s[1][kb], 0, 0, 0);
+                }
+            }
+
+            // ---- mask, online softmax ---------------------------------------------------
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                if (!full) {
+                    const int p = row_pos[rb];
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = t0 + kb * 16 + 4 * lg + i;
+                            const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
+                            s[rb][kb][i] = vis ? s[rb][kb][i] : kNeg;
+                        }
+                }
+                float mt = s[rb][0][0];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[rb][kb][i]);
+                mt = row_max4(mt);
+                const bool need = mt > m[rb] + kRescaleSlack;
+                if (__any(need)) {
+                    const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
+                    m[rb] = need ? mt : m[rb];
+                    lp[rb] *= f;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[rb][db] *= f;
+                }
+                float acc = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float pr = __builtin_amdgcn_exp2f(s[rb][kb][i] - m[rb]);
+                        if (!full) pr = s[rb][kb][i] == kNeg ? 0.f : pr;
+                        s[rb][kb][i] = pr;
+                        acc += pr;
+                    }
+                lp[rb] += acc;
+            }
+
+            // ---- O^T += V^T P^T -----------------------------------------------------------
+            bf16x8 pb[2][PVS];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int ps = 0; ps < PVS; ++ps)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pb[rb][ps][i] = (__bf16)s[rb][2 * ps][i];
+                        pb[rb][ps][4 + i] = (__bf16)s[rb][2 * ps + 1][i];
+                    }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int ps = 0; ps < PVS; ++ps) {
+                    const uint16_t* vp = vt_s + (db * 16 + l16) * VSTR + ps * 32 + 4 * lg;
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+                    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+                    const bf16x8 a = as_bf16x8(w);
+                    o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], o[0][db], 0, 0, 0);
+                    o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], o[1][db], 0, 0, 0);
+                }
+        }
+    }
+
+    // ---- normalise and write -------------------------------------------------------------
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float l = row_sum4(lp[rb]);
+        const int r = 32 * wave + 16 * rb + l16;
+        const int cl = c0 + r / G;
+        if (cl >= chunk) continue;
+        const int hq = h * G + r % G;
+        const float inv = 1.f / l;
+        uint16_t* orow = out + (((size_t)b * chunk + cl) * c.Hq + hq) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            u32x2 w;
+            const __bf16 e0 = (__bf16)(o[rb][db][0] * inv), e1 = (__bf16)(o[rb][db][1] * inv);
+            const __bf16 e2 = (__bf16)(o[rb][db][2] * inv), e3 = (__bf16)(o[rb][db][3] * inv);
+            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, e0) | ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, e2) | ((uint32_t)__builtin_bit_cast(uint16_t, e3) << 16);
+            *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * lg) = w;
+        }
+        if (lse != nullptr && lg == 0)
+            lse[((size_t)b * chunk + cl) * c.Hq + hq] = (m[rb] + __log2f(l)) * kLn2;
+    }
+}
+
+template <int D, int G>
+hipError_t launch_g(const DevCache& c, const void* v, void* out, float* lse, int chunk, int cur,
+                    hipStream_t s) {
+    constexpr int BQ = kRows / G;
+    const int n_qtiles = (chunk + BQ - 1) / BQ;
+    const int total = n_qtiles * c.Hkv * c.B;
+    const int grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(grid), dim3(kBlock), 0, s, c,
+                       (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DevCache& c, const void* v, void* out, float* lse, int chunk, int cur,
+                    hipStream_t s) {
+    switch (c.Hq / c.Hkv) {
+        case 1: return launch_g<D, 1>(c, v, out, lse, chunk, cur, s);
+        case 2: return launch_g<D, 2>(c, v, out, lse, chunk, cur, s);
+        case 4: return launch_g<D, 4>(c, v, out, lse, chunk, cur, s);
+        default: return launch_g<D, 8>(c, v, out, lse, chunk, cur, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_stage(const DevCache& c, const void* q, const void* k, int chunk, int cur,
+                                hipStream_t s) {
+    const size_t total = (size_t)c.B * chunk * (c.Hkv + c.Hq) * (c.D / 2);
+    const dim3 grid((unsigned)((total + kBlock - 1) / kBlock));
+    if (c.D == 128)
+        hipLaunchKernelGGL((stage_chunk_kernel<128>), grid, dim3(kBlock), 0, s, c,
+                           (const uint16_t*)q, (const uint16_t*)k, chunk, c.len[cur]);
+    else
+        hipLaunchKernelGGL((stage_chunk_kernel<64>), grid, dim3(kBlock), 0, s, c,
+                           (const uint16_t*)q, (const uint16_t*)k, chunk, c.len[cur]);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const DevCache& c, const void* v, void* out, float* lse, int chunk,
+                          int cur, hipStream_t s) {
+    return c.D == 128 ? launch_d<128>(c, v, out, lse, chunk, cur, s)
+                      : launch_d<64>(c, v, out, lse, chunk, cur, s);
 }
 
 }  // namespace psa

@@ -82,6 +82,7 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
     L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
     L->stage_k = off;  off = align_up(off + B * (size_t)d.max_chunk * Hkv * D * elem, A);
+    L->stage_q = off;  off = align_up(off + B * (size_t)d.max_chunk * Hq * D * 2, A);
     L->total = off;
     L->S = (int32_t)S;
     L->elem = (int32_t)elem;
@@ -215,6 +216,7 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.part_o = (float*)(base + L.part_o);
     d.part_ml = (float*)(base + L.part_ml);
     d.stage_k = base + L.stage_k;
+    d.stage_q = base + L.stage_q;
     d.B = desc->max_batch;
     d.Hq = desc->n_q_heads;
     d.Hkv = desc->n_kv_heads;
@@ -327,6 +329,7 @@ PSA_API int psa_prefill_attn(psa_cache* c, int32_t chunk, const void* q, const v
     if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
     if (c->desc.max_chunk < 1) return fail(PSA_ERR_ARG, "cache was created with max_chunk = 0");
     if (chunk < 1 || chunk > c->desc.max_chunk) return fail(PSA_ERR_ARG, "chunk must be in [1, max_chunk]");
+    if (c->desc.dtype != PSA_BF16) return fail(PSA_ERR_ARG, "chunked prefill needs bf16 storage");
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
         return fail(PSA_ERR_ARG, "q, k, v or out is NULL");
     const int B = c->desc.max_batch;
@@ -337,10 +340,10 @@ PSA_API int psa_prefill_attn(psa_cache* c, int32_t chunk, const void* q, const v
     hipStream_t s = (hipStream_t)stream;
     const int cur = c->cur;
     int rc = timed(c, PSA_K_PREFILL_STAGE, s, "prefill stage",
-                   [&] { return psa::launch_prefill_stage(c->dev, k, chunk, cur, s); });
+                   [&] { return psa::launch_prefill_stage(c->dev, q, k, chunk, cur, s); });
     if (rc != PSA_OK) return rc;
     rc = timed(c, PSA_K_PREFILL, s, "prefill attention",
-               [&] { return psa::launch_prefill(c->dev, q, v, out, lse, chunk, cur, s); });
+               [&] { return psa::launch_prefill(c->dev, v, out, lse, chunk, cur, s); });
     if (rc != PSA_OK) return rc;
     rc = timed(c, PSA_K_APPEND, s, "prefill commit", [&] {
         return psa::launch_append(c->dev, c->dev.stage_k, v, chunk, chunk, 0, 1, cur, s);

@@ -23,13 +23,14 @@ struct DevCache {
     double* inv_freq;    // [D/2] theta_i
     float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
-    void* stage_k;       // [B][Hkv][max_chunk][D] rotated prefill-chunk keys
+    void* stage_k;       // [B][max_chunk][Hkv][D] rotated prefill-chunk keys (stored bytes)
+    void* stage_q;       // [B][max_chunk][Hq][D] rotated, scaled prefill-chunk queries (bf16)
     int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits;
     float scale;
 };
 
 struct Layout {
-    size_t k, v, tags, state, inv_freq, part_o, part_ml, stage_k, total;
+    size_t k, v, tags, state, inv_freq, part_o, part_ml, stage_k, stage_q, total;
     int32_t S, elem, max_splits;
 };
 
@@ -46,9 +47,11 @@ hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tok
                                  int grid_splits, int cur, hipStream_t s);
 hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,
                         hipStream_t s);
-hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur,
-                                hipStream_t s);
-hipError_t launch_prefill(const DevCache& c, const void* q, const void* v, void* out, float* lse,
-                          int chunk, int cur, hipStream_t s);
+// Rotate a prefill chunk's keys (stored bytes) and queries (scaled, bf16) into the staging
+// buffers, then attend (bf16 storage only).
+hipError_t launch_prefill_stage(const DevCache& c, const void* q, const void* k, int chunk,
+                                int cur, hipStream_t s);
+hipError_t launch_prefill(const DevCache& c, const void* v, void* out, float* lse, int chunk,
+                          int cur, hipStream_t s);
 
 }  // namespace psa

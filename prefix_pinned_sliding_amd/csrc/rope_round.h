@@ -1,0 +1,61 @@
+// Device helpers shared by every kernel that produces stored keys: the float64 rotation
+// at an absolute position and the single rounding to the storage type. The append kernel
+// and the prefill staging kernel both use these, so a chunk's keys attended by prefill are
+// byte-identical to the keys the cache then holds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psa {
+
+__device__ __forceinline__ double bf16_bits_to_f64(uint16_t b) {
+    return (double)__uint_as_float((uint32_t)b << 16);
+}
+
+// float64 -> bfloat16 bits, one rounding to nearest, ties to even, on the float64 bit
+// fields: results below 2^-126 become bfloat16 subnormals, a carry out of the fraction
+// bumps the exponent, overflow gives infinity, NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+    const int e = (int)((u >> 52) & 0x7FF);
+    const uint64_t frac = u & ((1ull << 52) - 1);
+    if (e == 0x7FF) return sign | (frac ? 0x7FC0 : 0x7F80);
+    if (e == 0) return sign;                       // float64 zero or subnormal
+    const int E = e - 1023;
+    if (E >= -126) {
+        uint64_t body = ((uint64_t)(E + 127) << 7) | (frac >> 45);
+        const uint64_t rem = frac & ((1ull << 45) - 1);
+        const uint64_t half = 1ull << 44;
+        if (rem > half || (rem == half && (body & 1ull))) ++body;
+        if (body >= 0x7F80ull) body = 0x7F80ull;
+        return sign | (uint16_t)body;
+    }
+    const int sh = -E - 81;                        // leaves units of 2^-133
+    if (sh >= 64) return sign;
+    const uint64_t full = frac | (1ull << 52);
+    uint64_t kept = full >> sh;
+    const uint64_t rem = full & ((1ull << sh) - 1);
+    const uint64_t half = 1ull << (sh - 1);
+    if (rem > half || (rem == half && (kept & 1ull))) ++kept;
+    return sign | (uint16_t)kept;
+}
+
+// Rotate the pair (x, y) by the angle p * theta in float64: (x c - y s, x s + y c), the
+// angle, each product and each sum rounded on its own (no fused multiply-add).
+__device__ __forceinline__ void rotate_pair(double x, double y, int p, double theta, double* xr,
+                                            double* yr) {
+#pragma clang fp contract(off)
+    const double phi = (double)p * theta;
+    double sn, cs;
+    sincos(phi, &sn, &cs);
+    const double a = x * cs;
+    const double b = y * sn;
+    const double c = x * sn;
+    const double d = y * cs;
+    *xr = a - b;
+    *yr = c + d;
+}
+
+}  // namespace psa

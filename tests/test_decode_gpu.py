@@ -1,8 +1,14 @@
 """Decode attention on the GPU against the float64 oracle (masked full history).
 
 Tolerances: max|out - ref| <= 1e-5 for float32; for bfloat16, max-abs <= 2e-2 and
-||out - ref||_2 / ||ref||_2 <= 5e-3 over each call's checked outputs. lse (float32)
-within 1e-4 absolute. Full-size workloads are checked on sampled sequences (all heads)
+||out - ref||_2 / ||ref||_2 <= 5e-3 over each call's checked outputs.
+
+lse: the oracle rotates keys in float64 without rounding, the cache holds them rounded
+once to the storage type, so each logit carries an error of at most
+scale * sum_d |q_d| |k_d| * 2^-8 (half an ulp, relative 2^-8 at worst). For N(0,1)
+inputs at D = 128 that bound is about 0.03 for bfloat16 (typical errors ~1e-3) and
+about 1e-6 for float32 storage (2^-24). lse is a weighted mean of logits plus a log,
+so it inherits the same bound: checked at 2e-2 (bfloat16) and 1e-5 (float32). Full-size workloads are checked on sampled sequences (all heads)
 that the oracle computes one by one; every output is checked to be finite."""
 import numpy as np
 import pytest
@@ -29,6 +35,10 @@ def oracle_decode(wl, b, p, q_row):
                              wl.n_kv_heads, wl.rope_base, wl.scale)
 
 
+def lse_tol(dtype):
+    return 1e-5 if dtype == torch.float32 else 2e-2
+
+
 def step_and_check(c, wl, n_before, seqs=None, lse=True):
     """Append the token at p = n_before[b], decode it, compare chosen sequences."""
     B = wl.batch
@@ -48,7 +58,7 @@ def step_and_check(c, wl, n_before, seqs=None, lse=True):
         outs.append(o[b])
         refs.append(ref)
         if lse:
-            np.testing.assert_allclose(lse_t[b].cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
+            np.testing.assert_allclose(lse_t[b].cpu().numpy(), ref_lse, rtol=0, atol=lse_tol(wl.dtype))
     return np.stack(outs), np.stack(refs)
 
 
