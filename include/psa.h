@@ -164,9 +164,9 @@ int psa_export(psa_cache *cache, int32_t seq, void *k_host, void *v_host, int32_
  * sequence was never reset). Host only. */
 int64_t psa_seq_length(const psa_cache *cache, int32_t seq);
 
-/* Tokens per decode split (work unit of one workgroup); 0 restores the automatic
- * choice. Must be 0 or a multiple of 128. Results are the same up to float32
- * rounding order for any value. Host only. */
+/* Visible entries per decode split (the work unit of one workgroup); 0 restores the
+ * automatic choice. Must be 0 or >= 128. Results are the same up to float32 rounding
+ * order for any value. Host only. */
 int psa_set_split_tokens(psa_cache *cache, int32_t tokens);
 
 /* Kernel timing with HIP events recorded on the launch stream around each kernel.

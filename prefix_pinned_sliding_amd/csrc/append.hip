@@ -41,10 +41,12 @@ __global__ void seq_reset_kernel(int32_t* tags, int S, int32_t* len_cur, int32_t
     }
 }
 
-// One thread per (sequence b, token j, kv head h, rotation pair i). Token j of sequence b
-// has position p = len[b] + j. Slot: p < P_b -> prefix slot p; else ring slot
-// P_max + (p - P_b) mod W. A ring token that a later token of the same call overwrites
-// (p < len[b] + n_b - W) is not written, so the surviving writer of each slot is unique.
+// One thread per (sequence b, token j, KV head h, rotation pair i): a one-token append is
+// latency-bound, so every pair gets its own thread (each computes its angle's sin/cos).
+// Token j of sequence b has position p = len[b] + j. Slot: p < P_b -> prefix slot p;
+// else ring slot P_max + (p - P_b) mod W. A ring token that a later token of the same call
+// overwrites (p < len[b] + n_b - W) is not written, so the surviving writer of each slot is
+// unique.
 template <int DT, int D>
 __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typename Elem<DT>::T* k,
                                                         const typename Elem<DT>::T* v, int n_stride,
@@ -85,8 +87,9 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
         K[dst + i] = k[src + i];
         K[dst + i + H] = k[src + i + H];
     } else {
-        double xr, yr;
-        rotate_pair(to_f64(k[src + i]), to_f64(k[src + i + H]), p, c.inv_freq[i], &xr, &yr);
+        double sn, cs, xr, yr;
+        angle_sincos(p, c.inv_freq[i], &sn, &cs);
+        rotate_with(to_f64(k[src + i]), to_f64(k[src + i + H]), sn, cs, &xr, &yr);
         K[dst + i] = store_as(xr, (T*)nullptr);
         K[dst + i + H] = store_as(yr, (T*)nullptr);
     }

@@ -95,6 +95,36 @@ __device__ __forceinline__ float row_group_sum(float x) {
     return x;
 }
 
+#ifndef PSA_DECODE_ROUNDS
+#define PSA_DECODE_ROUNDS 2      // key rounds (of 64 / LPK keys) per wave per iteration
+#endif
+#ifndef PSA_DECODE_LPK_G2
+#define PSA_DECODE_LPK_G2 8      // lanes per key when a KV head serves one or two query heads
+#endif
+#ifndef PSA_DECODE_PIPELINE
+#define PSA_DECODE_PIPELINE 1    // 1: load the next iteration's K/V before computing this one
+#endif
+
+// Rotated, scaled query pair for position p (fp32 result). The angle p * theta_i is formed
+// and reduced modulo 2*pi in float64, then sin/cos are taken in float32: queries are never
+// stored, so float32 accuracy (~1e-7 relative) is all the logits need.
+__device__ __forceinline__ void rotate_query(float x, float y, int p, double theta, float sc,
+                                             float* xr, float* yr) {
+    const double phi = (double)p * theta;
+    const double two_pi = 6.283185307179586;
+    const double r = phi - two_pi * rint(phi * (1.0 / two_pi));
+    float sn, cs;
+    sincosf((float)r, &sn, &cs);
+    *xr = (x * cs - y * sn) * sc;
+    *yr = (x * sn + y * cs) * sc;
+}
+
+template <int DT, int D, int LPK, int U>
+struct KVTile {
+    static constexpr int CPL = (D / (16 / (int)sizeof(typename Elem<DT>::T))) / LPK;
+    u32x4 k[U][CPL], v[U][CPL];
+};
+
 template <int DT, int D, int G, int LPK>
 __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
                                                                 const typename Elem<DT>::T* q,
@@ -106,9 +136,11 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     constexpr int CPL = CPR / LPK;              // chunks per lane
     constexpr int EPL = CPL * EPC;              // elements per lane
     constexpr int KPW = 64 / LPK;               // keys per wave per load round
-    constexpr int U = 2;                        // load rounds per iteration
+    constexpr int U = PSA_DECODE_ROUNDS;
+    constexpr int STEP = kWaves * KPW * U;      // keys per workgroup iteration
     constexpr int ROWS = 4;                     // 16-lane rows per wave
     static_assert(CPL >= 1 && CPR % LPK == 0, "lane layout");
+    using Tile = KVTile<DT, D, LPK, U>;
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int n = len_cur[b];
@@ -129,19 +161,42 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     __shared__ float red_l[kWaves][ROWS][G];
     __shared__ float red_m[kWaves][G];
 
-    // Query heads h*G .. h*G+G-1 rotated at p = n - 1 (float64 angle and rotation), then
-    // scaled by scale * log2(e) so the softmax runs on exp2.
+    const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
+    const T* Kb = (const T*)c.k + head_off;
+    const T* Vb = (const T*)c.v + head_off;
+
+    // Logical entry i -> physical slot: the prefix rows, then the filled ring rows.
+    auto load = [&](Tile& t, int base_i) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = min(base_i + u * KPW + grp, i1 - 1);
+            const int slot = i < n_pre ? i : c.Pmax + (i - n_pre);
+            const u32x4* kp = reinterpret_cast<const u32x4*>(Kb + (size_t)slot * D);
+            const u32x4* vp = reinterpret_cast<const u32x4*>(Vb + (size_t)slot * D);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                t.k[u][cc] = __builtin_nontemporal_load(kp + cc * LPK + sub);
+                t.v[u][cc] = __builtin_nontemporal_load(vp + cc * LPK + sub);
+            }
+        }
+    };
+
+    // First K/V loads go out before the query set-up so that latency overlaps.
+    int base_i = i0 + wave * KPW * U;
+    Tile nxt;
+    if (base_i < i1) load(nxt, base_i);
+
     {
         const int p = n - 1;
         const float sc = c.scale * kLog2e;
         for (int idx = tid; idx < G * (D / 2); idx += kBlock) {
             const int g = idx / (D / 2), i = idx % (D / 2);
             const T* qp = q + ((size_t)b * c.Hq + h * G + g) * D;
-            const double x = to_f64(qp[i]), y = to_f64(qp[i + D / 2]);
-            double sn, cs;
-            sincos((double)p * c.inv_freq[i], &sn, &cs);
-            q_s[g][i] = (float)(x * cs - y * sn) * sc;
-            q_s[g][i + D / 2] = (float)(x * sn + y * cs) * sc;
+            float xr, yr;
+            rotate_query((float)to_f64(qp[i]), (float)to_f64(qp[i + D / 2]), p, c.inv_freq[i], sc,
+                         &xr, &yr);
+            q_s[g][i] = xr;
+            q_s[g][i + D / 2] = yr;
         }
     }
     __syncthreads();
@@ -163,40 +218,26 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
         for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
 
-    const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
-    const T* Kb = (const T*)c.k + head_off;
-    const T* Vb = (const T*)c.v + head_off;
+    while (base_i < i1) {
+        Tile cur = nxt;
+        const int cur_i = base_i;
+        base_i += STEP;
+        if (PSA_DECODE_PIPELINE && base_i < i1) load(nxt, base_i);
 
-    for (int base_i = i0 + wave * KPW * U; base_i < i1; base_i += kWaves * KPW * U) {
-        u32x4 kw[U][CPL], vw[U][CPL];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = base_i + u * KPW + grp;
-            ok[u] = i < i1;
-            const int ii = ok[u] ? i : i1 - 1;
-            const int slot = ii < n_pre ? ii : c.Pmax + (ii - n_pre);
-            const u32x4* kp = reinterpret_cast<const u32x4*>(Kb + (size_t)slot * D);
-            const u32x4* vp = reinterpret_cast<const u32x4*>(Vb + (size_t)slot * D);
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                kw[u][cc] = __builtin_nontemporal_load(kp + cc * LPK + sub);
-                vw[u][cc] = __builtin_nontemporal_load(vp + cc * LPK + sub);
-            }
-        }
         float s[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const bool ok = cur_i + u * KPW + grp < i1;
             float kf[EPL];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) unpack(kw[u][cc], kf + cc * EPC, (T*)nullptr);
+            for (int cc = 0; cc < CPL; ++cc) unpack(cur.k[u][cc], kf + cc * EPC, (T*)nullptr);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) d += qr[g][e] * kf[e];
                 d = key_sum<LPK>(d);
-                s[u][g] = ok[u] ? d : -INFINITY;
+                s[u][g] = ok ? d : -INFINITY;
             }
         }
 #pragma unroll
@@ -217,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
         for (int u = 0; u < U; ++u) {
             float vf[EPL];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) unpack(vw[u][cc], vf + cc * EPC, (T*)nullptr);
+            for (int cc = 0; cc < CPL; ++cc) unpack(cur.v[u][cc], vf + cc * EPC, (T*)nullptr);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float pr = __builtin_amdgcn_exp2f(s[u][g] - m[g]);
@@ -226,6 +267,7 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
                 for (int e = 0; e < EPL; ++e) acc[g][e] += pr * vf[e];
             }
         }
+        if (!PSA_DECODE_PIPELINE && base_i < i1) load(nxt, base_i);
     }
 
     // Combine: lane groups in a row share m, so sum them; rows and waves go through LDS.
@@ -309,7 +351,7 @@ hipError_t launch_partial_g(const DevCache& c, const void* q, int split_tokens, 
     // Lanes per key: enough that q and the accumulators of G heads fit in registers,
     // never more than the 16-byte chunks in a row.
     constexpr int CPR = D / (16 / (int)sizeof(typename Elem<DT>::T));
-    constexpr int PREF = G <= 2 ? 4 : (G == 4 ? 8 : 16);
+    constexpr int PREF = G <= 2 ? PSA_DECODE_LPK_G2 : (G == 4 ? 8 : 16);
     constexpr int LPK = PREF < CPR ? PREF : CPR;
     const dim3 grid(grid_splits, c.Hkv, c.B);
     hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK>), grid, dim3(kBlock), 0, s, c,
@@ -328,6 +370,34 @@ hipError_t launch_partial_d(const DevCache& c, const void* q, int split_tokens, 
     }
 }
 
+
+template <int DT, int D, int G>
+int wgs_per_cu_g() {
+    constexpr int CPR = D / (16 / (int)sizeof(typename Elem<DT>::T));
+    constexpr int PREF = G <= 2 ? PSA_DECODE_LPK_G2 : (G == 4 ? 8 : 16);
+    constexpr int LPK = PREF < CPR ? PREF : CPR;
+    static int cached = 0;
+    if (cached == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void*>(&decode_partial_kernel<DT, D, G, LPK>), kBlock,
+                0) != hipSuccess || n < 1)
+            n = 1;
+        cached = n;
+    }
+    return cached;
+}
+
+template <int DT, int D>
+int wgs_per_cu_d(int G) {
+    switch (G) {
+        case 1: return wgs_per_cu_g<DT, D, 1>();
+        case 2: return wgs_per_cu_g<DT, D, 2>();
+        case 4: return wgs_per_cu_g<DT, D, 4>();
+        default: return wgs_per_cu_g<DT, D, 8>();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
@@ -337,6 +407,18 @@ hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tok
                           : launch_partial_d<PSA_BF16, 64>(c, q, split_tokens, grid_splits, cur, s);
     return c.D == 128 ? launch_partial_d<PSA_F32, 128>(c, q, split_tokens, grid_splits, cur, s)
                       : launch_partial_d<PSA_F32, 64>(c, q, split_tokens, grid_splits, cur, s);
+}
+
+int decode_resident_wgs(const DevCache& c) {
+    const int G = c.Hq / c.Hkv;
+    const int per_cu = c.dtype == PSA_BF16
+                           ? (c.D == 128 ? wgs_per_cu_d<PSA_BF16, 128>(G) : wgs_per_cu_d<PSA_BF16, 64>(G))
+                           : (c.D == 128 ? wgs_per_cu_d<PSA_F32, 128>(G) : wgs_per_cu_d<PSA_F32, 64>(G));
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 1;
+    return per_cu * cus;
 }
 
 hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,

@@ -34,6 +34,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+#ifndef PSA_PREFILL_PIPELINE
+#define PSA_PREFILL_PIPELINE 1   // 1: fetch the next tile's K/V while computing this one
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kRows = 128;              // rows (position x head) per workgroup
@@ -48,39 +52,48 @@ __device__ __forceinline__ uint16_t q_to_bf16(double x) { return f64_to_bf16_bit
 
 // Stage a chunk: keys rotated at their absolute positions and rounded once (the bytes the
 // cache will hold), queries rotated, multiplied by scale * log2(e) and rounded to bf16.
-// One thread per (sequence, token, head, pair); heads [0, Hkv) are keys, the rest queries.
+// One thread per (sequence, token, group of kStageHeads heads, pair): the angle's sin/cos
+// is computed once per group; heads [0, Hkv) are keys, [Hkv, Hkv + Hq) queries.
+constexpr int kStageHeads = 4;
+
 template <int D>
 __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const uint16_t* q,
                                                              const uint16_t* k, int chunk,
                                                              const int32_t* __restrict__ len_cur) {
     constexpr int H = D / 2;
     const int heads = c.Hkv + c.Hq;
+    const int groups = (heads + kStageHeads - 1) / kStageHeads;
     const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    const size_t total = (size_t)c.B * chunk * heads * H;
+    const size_t total = (size_t)c.B * chunk * groups * H;
     if (idx >= total) return;
     const int i = (int)(idx % H);
     size_t r = idx / H;
-    const int hh = (int)(r % heads);
-    r /= heads;
+    const int grp = (int)(r % groups);
+    r /= groups;
     const int j = (int)(r % chunk);
     const int b = (int)(r / chunk);
     const int p = len_cur[b] + j;
-    const bool is_key = hh < c.Hkv;
-    const size_t off = is_key ? (((size_t)b * chunk + j) * c.Hkv + hh) * D
-                              : (((size_t)b * chunk + j) * c.Hq + (hh - c.Hkv)) * D;
-    const uint16_t* src = is_key ? k : q;
-    double xr, yr;
-    rotate_pair(bf16_bits_to_f64(src[off + i]), bf16_bits_to_f64(src[off + i + H]), p,
-                c.inv_freq[i], &xr, &yr);
-    if (is_key) {
-        uint16_t* out = (uint16_t*)c.stage_k;
-        out[off + i] = f64_to_bf16_bits(xr);
-        out[off + i + H] = f64_to_bf16_bits(yr);
-    } else {
-        const double sc = (double)c.scale * (double)kLog2e;
-        uint16_t* out = (uint16_t*)c.stage_q;
-        out[off + i] = q_to_bf16(xr * sc);
-        out[off + i + H] = q_to_bf16(yr * sc);
+    double sn, cs;
+    angle_sincos(p, c.inv_freq[i], &sn, &cs);
+    const size_t tok = (size_t)b * chunk + j;
+    const double sc = (double)c.scale * (double)kLog2e;
+    const int h_end = min(heads, (grp + 1) * kStageHeads);
+#pragma unroll
+    for (int hh = grp * kStageHeads; hh < h_end; ++hh) {
+        const bool is_key = hh < c.Hkv;
+        const size_t off = is_key ? (tok * c.Hkv + hh) * D : (tok * c.Hq + (hh - c.Hkv)) * D;
+        const uint16_t* src = is_key ? k : q;
+        double xr, yr;
+        rotate_with(bf16_bits_to_f64(src[off + i]), bf16_bits_to_f64(src[off + i + H]), sn, cs, &xr, &yr);
+        if (is_key) {
+            uint16_t* ko = (uint16_t*)c.stage_k;
+            ko[off + i] = f64_to_bf16_bits(xr);
+            ko[off + i + H] = f64_to_bf16_bits(yr);
+        } else {
+            uint16_t* qo = (uint16_t*)c.stage_q;
+            qo[off + i] = q_to_bf16(xr * sc);
+            qo[off + i + H] = q_to_bf16(yr * sc);
+        }
     }
 }
 
@@ -100,6 +113,104 @@ __device__ __forceinline__ float row_sum4(float x) {
     return x;
 }
 
+// The three key ranges of a workgroup and the first row's window start; `next` steps
+// (seg, t0) to the next tile that some row of the workgroup sees.
+struct Walk {
+    int hi0, lo1, hi1, lo2, hi2, P, win_lo;
+    __device__ int lo(int seg) const { return seg == 1 ? lo1 : (seg == 2 ? lo2 : 0); }
+    __device__ int hi(int seg) const { return seg == 0 ? hi0 : (seg == 1 ? hi1 : hi2); }
+};
+
+template <int BN>
+__device__ __forceinline__ bool walk_next(const Walk& w, int& seg, int& t0) {
+    t0 += BN;
+    while (seg < 3) {
+        const int hi = w.hi(seg);
+        if (t0 >= hi) {
+            ++seg;
+            if (seg < 3) t0 = w.lo(seg);
+            continue;
+        }
+        const int t1 = min(t0 + BN, hi);
+        // no row sees any key: all past the prefix and older than the first row's window
+        if (t0 >= w.P && t1 - 1 < w.win_lo) {
+            t0 += BN;
+            continue;
+        }
+        return true;
+    }
+    return false;
+}
+
+// Where the K and V rows of position j live for key range `seg`.
+struct TileSrc {
+    const uint16_t *k_cache, *v_cache, *k_chunk, *v_chunk;
+    size_t chunk_row0;   // b * chunk
+    int n, P, W, Pmax, Hkv, h;
+    __device__ size_t cache_row(int seg, int j) const {
+        return seg == 0 ? (size_t)j : (size_t)(Pmax + (j - P) % W);
+    }
+    __device__ size_t chunk_off(int j) const { return ((chunk_row0 + (j - n)) * Hkv + h); }
+};
+
+// This thread's share of a tile into registers: KLD 16-byte chunks of K rows, and a block
+// of 4 keys x 8 dims of V. Positions past t1 read the last valid row (masked later).
+template <int D, int BN, int NT>
+__device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, int t1, int tid,
+                                           u32x4* kreg, u32x4* vreg) {
+    constexpr int CPR = D / 8;
+    constexpr int KLD = (BN * CPR) / NT;
+#pragma unroll
+    for (int rr = 0; rr < KLD; ++rr) {
+        const int ci = tid + NT * rr;
+        const int kk = ci / CPR, col = ci % CPR;
+        const int j = min(t0 + kk, t1 - 1);
+        const uint16_t* row = seg < 2 ? s.k_cache + s.cache_row(seg, j) * D
+                                      : s.k_chunk + s.chunk_off(j) * D;
+        kreg[rr] = *reinterpret_cast<const u32x4*>(row + col * 8);
+    }
+    const int dc = tid % CPR, kq = tid / CPR;
+    if (kq < BN / 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = min(t0 + 4 * kq + e, t1 - 1);
+            const uint16_t* row = seg < 2 ? s.v_cache + s.cache_row(seg, j) * D
+                                          : s.v_chunk + s.chunk_off(j) * D;
+            vreg[e] = *reinterpret_cast<const u32x4*>(row + dc * 8);
+        }
+    }
+}
+
+// Registers -> LDS: K rows as they are, V transposed (4 keys x 8 dims -> 8 rows of V^T
+// holding 4 consecutive keys each).
+template <int D, int BN, int NT, int KSTR, int VSTR>
+__device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int tid,
+                                           const u32x4* kreg, const u32x4* vreg) {
+    constexpr int CPR = D / 8;
+    constexpr int KLD = (BN * CPR) / NT;
+#pragma unroll
+    for (int rr = 0; rr < KLD; ++rr) {
+        const int ci = tid + NT * rr;
+        const int kk = ci / CPR, col = ci % CPR;
+        *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
+    }
+    const int dc = tid % CPR, kq = tid / CPR;
+    if (kq < BN / 4) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t a0 = vreg[0][x], a1 = vreg[1][x], a2 = vreg[2][x], a3 = vreg[3][x];
+            u32x2 lo, hi;   // dims 2x (low halves) and 2x + 1 (high halves)
+            lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+            lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+            hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+            hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+            const int d0 = dc * 8 + 2 * x;
+            *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + 4 * kq) = lo;
+            *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + 4 * kq) = hi;
+        }
+    }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
                                                             uint16_t* __restrict__ out,
@@ -114,6 +225,7 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
     constexpr int VSTR = kBN + 4;         // LDS row stride of V^T (elements)
     constexpr int CPR = D / 8;            // 16-byte chunks per row
+    constexpr int KLD = (kBN * CPR) / kBlock;
 
     __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
@@ -171,147 +283,112 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     const uint16_t* Vc = (const uint16_t*)c.v + head_off;
     const uint16_t* Ks = (const uint16_t*)c.stage_k;
 
-    // segment bounds in position space
+    // Key ranges in position space: 0 = prefix (cache), 1 = still-visible ring (cache),
+    // 2 = the chunk (staged keys, input values).
     const int nA = min(n, P);
-    const int jB0 = max(P, p_lo - W + 1);
-    const int seg_lo[3] = {0, n > P ? jB0 : n, n};
-    const int seg_hi[3] = {nA, n, p_hi + 1};
+    const int lo1 = n > P ? max(P, p_lo - W + 1) : n;
+    const int lo2 = n, hi2 = p_hi + 1;
+    const Walk wk{nA, lo1, n, lo2, hi2, P, p_lo - W + 1};
+    const TileSrc src{Kc, Vc, Ks, v_in, (size_t)b * chunk, n, P, W, c.Pmax, c.Hkv, h};
 
+    u32x4 kreg[KLD], vreg[4];
+    int seg = 0, t0 = -kBN;
+    bool have = walk_next<kBN>(wk, seg, t0);
+    if (PSA_PREFILL_PIPELINE && have)
+        fetch_tile<D, kBN, kBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
 #pragma unroll 1
-    for (int seg = 0; seg < 3; ++seg) {
-#pragma unroll 1
-        for (int t0 = seg_lo[seg]; t0 < seg_hi[seg]; t0 += kBN) {
-            const int t1 = min(t0 + kBN, seg_hi[seg]);
-            // no row sees any key of the tile: all keys past the prefix and older than the
-            // window of the first row
-            if (t0 >= P && t1 - 1 < p_lo - W + 1) continue;
-            const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) &&
-                              (t1 - 1 < P || t0 >= p_hi - W + 1);
+    while (have) {
+        const int cseg = seg, ct0 = t0;
+        const int t1 = min(ct0 + kBN, wk.hi(cseg));
+        const bool full = (ct0 + kBN == t1) && (t1 - 1 <= p_lo) &&
+                          (t1 - 1 < P || ct0 >= p_hi - W + 1);
+        __syncthreads();                  // the previous tile's LDS reads are done
+        if (!PSA_PREFILL_PIPELINE) fetch_tile<D, kBN, kBlock>(src, cseg, ct0, t1, tid, kreg, vreg);
+        stage_tile<D, kBN, kBlock, KSTR, VSTR>(k_s, vt_s, tid, kreg, vreg);
+        have = walk_next<kBN>(wk, seg, t0);
+        if (PSA_PREFILL_PIPELINE && have)   // in flight while this tile is computed
+            fetch_tile<D, kBN, kBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+        __syncthreads();
 
-            // ---- stage the tile: K rows as is, V transposed -----------------------------
-            __syncthreads();
+        // ---- S^T = K Q^T ----------------------------------------------------------------
+        f32x4 s[2][KB];
 #pragma unroll
-            for (int rr = 0; rr < (kBN * CPR) / kBlock; ++rr) {
-                const int ci = tid + kBlock * rr;
-                const int kk = ci / CPR, col = ci % CPR;
-                const int j = min(t0 + kk, t1 - 1);
-                const uint16_t* src;
-                if (seg == 0) src = Kc + (size_t)j * D;
-                else if (seg == 1) src = Kc + (size_t)(c.Pmax + (j - P) % W) * D;
-                else src = Ks + (((size_t)b * chunk + (j - n)) * c.Hkv + h) * D;
-                *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) =
-                    *reinterpret_cast<const u32x4*>(src + col * 8);
+        for (int kb = 0; kb < KB; ++kb) {
+            s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = as_bf16x8(
+                    *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
+                s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0][ks], s[0][kb], 0, 0, 0);
+                s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1][ks], s[1][kb], 0, 0, 0);
             }
-            {
-                const int dc = tid % CPR, kq = tid / CPR;
-                if (kq < kBN / 4) {
-                    u32x4 w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = min(t0 + 4 * kq + e, t1 - 1);
-                        const uint16_t* src;
-                        if (seg == 0) src = Vc + (size_t)j * D;
-                        else if (seg == 1) src = Vc + (size_t)(c.Pmax + (j - P) % W) * D;
-                        else src = v_in + (((size_t)b * chunk + (j - n)) * c.Hkv + h) * D;
-                        w[e] = *reinterpret_cast<const u32x4*>(src + dc * 8);
-                    }
-                    // 4 keys x 8 dims -> 8 rows of V^T with 4 consecutive keys each
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const uint32_t a0 = w[0][x], a1 = w[1][x], a2 = w[2][x], a3 = w[3][x];
-                        u32x2 lo, hi;   // dims 2x (low halves) and 2x + 1 (high halves)
-                        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-                        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-                        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-                        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-                        const int d0 = dc * 8 + 2 * x;
-                        *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + 4 * kq) = lo;
-                        *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + 4 * kq) = hi;
-                    }
-                }
-            }
-            __syncthreads();
-
-            // ---- S^T = K Q^T ------------------------------------------------------------
-            f32x4 s[2][KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = as_bf16x8(
-                        *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
-                    s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0][ks], s[0][kb], 0, 0, 0);
-                    s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1][ks], s[1][kb], 0, 0, 0);
-                }
-            }
-
-            // ---- mask, online softmax ---------------------------------------------------
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                if (!full) {
-                    const int p = row_pos[rb];
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int j = t0 + kb * 16 + 4 * lg + i;
-                            const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
-                            s[rb][kb][i] = vis ? s[rb][kb][i] : kNeg;
-                        }
-                }
-                float mt = s[rb][0][0];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[rb][kb][i]);
-                mt = row_max4(mt);
-                const bool need = mt > m[rb] + kRescaleSlack;
-                if (__any(need)) {
-                    const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
-                    m[rb] = need ? mt : m[rb];
-                    lp[rb] *= f;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) o[rb][db] *= f;
-                }
-                float acc = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float pr = __builtin_amdgcn_exp2f(s[rb][kb][i] - m[rb]);
-                        if (!full) pr = s[rb][kb][i] == kNeg ? 0.f : pr;
-                        s[rb][kb][i] = pr;
-                        acc += pr;
-                    }
-                lp[rb] += acc;
-            }
-
-            // ---- O^T += V^T P^T -----------------------------------------------------------
-            bf16x8 pb[2][PVS];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int ps = 0; ps < PVS; ++ps)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pb[rb][ps][i] = (__bf16)s[rb][2 * ps][i];
-                        pb[rb][ps][4 + i] = (__bf16)s[rb][2 * ps + 1][i];
-                    }
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int ps = 0; ps < PVS; ++ps) {
-                    const uint16_t* vp = vt_s + (db * 16 + l16) * VSTR + ps * 32 + 4 * lg;
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-                    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                    const bf16x8 a = as_bf16x8(w);
-                    o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], o[0][db], 0, 0, 0);
-                    o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], o[1][db], 0, 0, 0);
-                }
         }
+
+        // ---- mask, online softmax -------------------------------------------------------
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            if (!full) {
+                const int p = row_pos[rb];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = ct0 + kb * 16 + 4 * lg + i;
+                        const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
+                        s[rb][kb][i] = vis ? s[rb][kb][i] : kNeg;
+                    }
+            }
+            float mt = s[rb][0][0];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[rb][kb][i]);
+            mt = row_max4(mt);
+            const bool need = mt > m[rb] + kRescaleSlack;
+            if (__any(need)) {
+                const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
+                m[rb] = need ? mt : m[rb];
+                lp[rb] *= f;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[rb][db] *= f;
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float pr = __builtin_amdgcn_exp2f(s[rb][kb][i] - m[rb]);
+                    if (!full) pr = s[rb][kb][i] == kNeg ? 0.f : pr;
+                    s[rb][kb][i] = pr;
+                    acc += pr;
+                }
+            lp[rb] += acc;
+        }
+
+        // ---- O^T += V^T P^T -------------------------------------------------------------
+        bf16x8 pb[2][PVS];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ps = 0; ps < PVS; ++ps)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pb[rb][ps][i] = (__bf16)s[rb][2 * ps][i];
+                    pb[rb][ps][4 + i] = (__bf16)s[rb][2 * ps + 1][i];
+                }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int ps = 0; ps < PVS; ++ps) {
+                const uint16_t* vp = vt_s + (db * 16 + l16) * VSTR + ps * 32 + 4 * lg;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+                const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+                const bf16x8 a = as_bf16x8(w);
+                o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], o[0][db], 0, 0, 0);
+                o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], o[1][db], 0, 0, 0);
+            }
     }
 
     // ---- normalise and write -------------------------------------------------------------
@@ -365,7 +442,8 @@ hipError_t launch_d(const DevCache& c, const void* v, void* out, float* lse, int
 
 hipError_t launch_prefill_stage(const DevCache& c, const void* q, const void* k, int chunk, int cur,
                                 hipStream_t s) {
-    const size_t total = (size_t)c.B * chunk * (c.Hkv + c.Hq) * (c.D / 2);
+    const int groups = (c.Hkv + c.Hq + kStageHeads - 1) / kStageHeads;
+    const size_t total = (size_t)c.B * chunk * groups * (c.D / 2);
     const dim3 grid((unsigned)((total + kBlock - 1) / kBlock));
     if (c.D == 128)
         hipLaunchKernelGGL((stage_chunk_kernel<128>), grid, dim3(kBlock), 0, s, c,

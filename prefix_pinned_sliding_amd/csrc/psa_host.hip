@@ -12,6 +12,8 @@
 
 #define PSA_API extern "C" __attribute__((visibility("default")))
 
+
+
 namespace {
 
 thread_local std::string g_err;
@@ -39,6 +41,7 @@ struct psa_cache {
     std::vector<int64_t> len;      // host mirror of history lengths
     std::vector<int32_t> pre;      // host mirror of P_b; -1 = never reset
     int32_t split_tokens;          // 0 = automatic
+    int resident_wgs;              // decode workgroups resident at once (0 = not yet queried)
     bool profiling;
     std::vector<EventPair> pending;
     double total_ms[PSA_K_COUNT];
@@ -128,15 +131,23 @@ int64_t visible_count(const psa_cache* c, int b) {
     return n_pre + n_win;
 }
 
-// Automatic split length: the smallest multiple of 256 that keeps the decode grid at or
-// below about 16 workgroups per compute unit of work, but no shorter than 256 tokens.
-int auto_split_tokens(const psa_cache* c) {
-    int64_t total = 0;
-    for (int b = 0; b < c->desc.max_batch; ++b) total += visible_count(c, b);
-    const int64_t target_wgs = 4096;
-    int64_t per = (total * c->desc.n_kv_heads + target_wgs - 1) / target_wgs;
-    int64_t L = 256;
-    while (L < per && L < (int64_t)1 << 20) L += 256;
+// Automatic split length. Split the longest sequence into ns pieces with ns chosen so the
+// grid is about two rounds of the workgroups that fit on the device at once (measured:
+// longer splits amortise each workgroup's set-up and final reduction, and whole rounds
+// avoid a ragged tail); the pieces are equal so no split is a short remainder. Never
+// shorter than kSplitGranule entries.
+int auto_split_tokens(psa_cache* c) {
+    int64_t longest = 1;
+    for (int b = 0; b < c->desc.max_batch; ++b) {
+        const int64_t t = visible_count(c, b);
+        if (t > longest) longest = t;
+    }
+    if (c->resident_wgs == 0) c->resident_wgs = psa::decode_resident_wgs(c->dev);
+    const int64_t pairs = (int64_t)c->desc.max_batch * c->desc.n_kv_heads;
+    int64_t ns = (2 * (int64_t)c->resident_wgs) / pairs;
+    if (ns < 1) ns = 1;
+    int64_t L = (longest + ns - 1) / ns;
+    if (L < psa::kSplitGranule) L = psa::kSplitGranule;
     return (int)L;
 }
 
@@ -197,6 +208,7 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     c->len.assign(desc->max_batch, 0);
     c->pre.assign(desc->max_batch, -1);
     c->split_tokens = 0;
+    c->resident_wgs = 0;
     c->profiling = false;
     for (int i = 0; i < PSA_K_COUNT; ++i) {
         c->total_ms[i] = 0.0;
@@ -409,8 +421,8 @@ PSA_API int64_t psa_seq_length(const psa_cache* c, int32_t seq) {
 
 PSA_API int psa_set_split_tokens(psa_cache* c, int32_t tokens) {
     if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
-    if (tokens < 0 || tokens % psa::kSplitGranule != 0)
-        return fail(PSA_ERR_ARG, "split tokens must be 0 or a positive multiple of 128");
+    if (tokens != 0 && tokens < psa::kSplitGranule)
+        return fail(PSA_ERR_ARG, "split tokens must be 0 (automatic) or at least 128");
     c->split_tokens = tokens;
     return PSA_OK;
 }

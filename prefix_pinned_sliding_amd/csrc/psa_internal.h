@@ -45,6 +45,8 @@ hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_
                          int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s);
 hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
                                  int grid_splits, int cur, hipStream_t s);
+// Workgroups of the decode kernel (for this cache's shape) that fit on the device at once.
+int decode_resident_wgs(const DevCache& c);
 hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,
                         hipStream_t s);
 // Rotate a prefill chunk's keys (stored bytes) and queries (scaled, bf16) into the staging

@@ -42,14 +42,19 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
     return sign | (uint16_t)kept;
 }
 
-// Rotate the pair (x, y) by the angle p * theta in float64: (x c - y s, x s + y c), the
-// angle, each product and each sum rounded on its own (no fused multiply-add).
-__device__ __forceinline__ void rotate_pair(double x, double y, int p, double theta, double* xr,
-                                            double* yr) {
+// sin and cos of the angle p * theta, the angle rounded once in float64.
+__device__ __forceinline__ void angle_sincos(int p, double theta, double* sn, double* cs) {
 #pragma clang fp contract(off)
     const double phi = (double)p * theta;
-    double sn, cs;
-    sincos(phi, &sn, &cs);
+    sincos(phi, sn, cs);
+}
+
+// Rotate the pair (x, y) by an angle with sine sn and cosine cs in float64:
+// (x c - y s, x s + y c), each product and each sum rounded on its own (no fused
+// multiply-add).
+__device__ __forceinline__ void rotate_with(double x, double y, double sn, double cs, double* xr,
+                                            double* yr) {
+#pragma clang fp contract(off)
     const double a = x * cs;
     const double b = y * sn;
     const double c = x * sn;
