@@ -33,6 +33,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 #ifndef PSA_PREFILL_PIPELINE
 #define PSA_PREFILL_PIPELINE 1   // 1: fetch the next tile's K/V while computing this one
@@ -44,7 +45,8 @@ constexpr int kRows = 128;              // rows (position x head) per workgroup
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNeg = -1.0e30f;        // logit of a masked pair (finite: no inf - inf)
+constexpr float kNeg = -1.0e30f;        // initial running max (finite: -inf - kNeg = -inf)
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kRescaleSlack = 8.0f;
 
 // float64 -> bfloat16 for staged queries: the same single rounding as stored keys.
@@ -147,42 +149,70 @@ struct TileSrc {
     const uint16_t *k_cache, *v_cache, *k_chunk, *v_chunk;
     size_t chunk_row0;   // b * chunk
     int n, P, W, Pmax, Hkv, h;
-    __device__ size_t cache_row(int seg, int j) const {
-        return seg == 0 ? (size_t)j : (size_t)(Pmax + (j - P) % W);
-    }
-    __device__ size_t chunk_off(int j) const { return ((chunk_row0 + (j - n)) * Hkv + h); }
 };
 
-// This thread's share of a tile into registers: KLD 16-byte chunks of K rows, and a block
-// of 4 keys x 8 dims of V. Positions past t1 read the last valid row (masked later).
+// This thread's share of a tile into registers: KLD 16-byte chunks of K rows (lanes along
+// a row), and a block of 4 keys x 8 dims of V (lanes along the keys). Positions past t1
+// read the last valid row (masked later). Each tile gets one base pointer per operand;
+// rows are 32-bit offsets from it: consecutive rows for the prefix and the chunk, the ring
+// slot (reduced modulo W once per tile, then one wrap) for the window.
 template <int D, int BN, int NT>
 __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, int t1, int tid,
                                            u32x4* kreg, u32x4* vreg) {
     constexpr int CPR = D / 8;
     constexpr int KLD = (BN * CPR) / NT;
+    const int last = t1 - 1 - t0;
+    const uint16_t* kb;
+    const uint16_t* vb;
+    int stride, ring0 = 0;
+    if (seg == 2) {
+        const size_t o = ((s.chunk_row0 + (size_t)(t0 - s.n)) * s.Hkv + s.h) * D;
+        kb = s.k_chunk + o;
+        vb = s.v_chunk + o;
+        stride = s.Hkv * D;
+    } else if (seg == 1) {
+        kb = s.k_cache + (size_t)s.Pmax * D;
+        vb = s.v_cache + (size_t)s.Pmax * D;
+        stride = D;
+        ring0 = (t0 - s.P) % s.W;
+    } else {
+        kb = s.k_cache + (size_t)t0 * D;
+        vb = s.v_cache + (size_t)t0 * D;
+        stride = D;
+    }
+    auto row = [&](int off) -> int {   // row index relative to the tile's base pointer
+        if (seg != 1) return off;
+        const int r = ring0 + off;
+        return s.W >= BN ? (r >= s.W ? r - s.W : r) : r % s.W;
+    };
 #pragma unroll
     for (int rr = 0; rr < KLD; ++rr) {
         const int ci = tid + NT * rr;
         const int kk = ci / CPR, col = ci % CPR;
-        const int j = min(t0 + kk, t1 - 1);
-        const uint16_t* row = seg < 2 ? s.k_cache + s.cache_row(seg, j) * D
-                                      : s.k_chunk + s.chunk_off(j) * D;
-        kreg[rr] = *reinterpret_cast<const u32x4*>(row + col * 8);
+        const uint32_t e = __umul24((uint32_t)row(min(kk, last)), (uint32_t)stride) + col * 8;
+        kreg[rr] = *reinterpret_cast<const u32x4*>(kb + e);
     }
-    const int dc = tid % CPR, kq = tid / CPR;
-    if (kq < BN / 4) {
+    const int kq = tid % (BN / 4), dc = tid / (BN / 4);
+    if (dc < CPR) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = min(t0 + 4 * kq + e, t1 - 1);
-            const uint16_t* row = seg < 2 ? s.v_cache + s.cache_row(seg, j) * D
-                                          : s.v_chunk + s.chunk_off(j) * D;
-            vreg[e] = *reinterpret_cast<const u32x4*>(row + dc * 8);
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e = __umul24((uint32_t)row(min(4 * kq + q, last)), (uint32_t)stride) + dc * 8;
+            vreg[q] = *reinterpret_cast<const u32x4*>(vb + e);
         }
     }
 }
 
+// V^T column of the first of 4 keys 4kq .. 4kq + 3. Within each 32-key group, lane group g
+// of an MFMA k-step needs keys 4g .. 4g+3 and 16 + 4g .. 16 + 4g + 3 (the accumulator
+// layout of S^T); storing those 8 keys side by side at columns 8g .. 8g + 7 turns the
+// operand into one aligned 16-byte LDS read.
+__device__ __forceinline__ int vt_col(int kq) {
+    const int q = kq & 7;
+    return 32 * (kq >> 3) + (q < 4 ? 8 * q : 8 * (q - 4) + 4);
+}
+
 // Registers -> LDS: K rows as they are, V transposed (4 keys x 8 dims -> 8 rows of V^T
-// holding 4 consecutive keys each).
+// holding 4 keys each, columns permuted by vt_col).
 template <int D, int BN, int NT, int KSTR, int VSTR>
 __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int tid,
                                            const u32x4* kreg, const u32x4* vreg) {
@@ -194,8 +224,8 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int ti
         const int kk = ci / CPR, col = ci % CPR;
         *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
     }
-    const int dc = tid % CPR, kq = tid / CPR;
-    if (kq < BN / 4) {
+    const int kq = tid % (BN / 4), dc = tid / (BN / 4);
+    if (dc < CPR) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const uint32_t a0 = vreg[0][x], a1 = vreg[1][x], a2 = vreg[2][x], a3 = vreg[3][x];
@@ -205,8 +235,9 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int ti
             hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
             hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
             const int d0 = dc * 8 + 2 * x;
-            *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + 4 * kq) = lo;
-            *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + 4 * kq) = hi;
+            const int col = vt_col(kq);
+            *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + col) = lo;
+            *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + col) = hi;
         }
     }
 }
@@ -223,7 +254,7 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     constexpr int KB = kBN / 16;          // key blocks per tile
     constexpr int PVS = kBN / 32;         // k-steps of O^T = V^T P^T
     constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
-    constexpr int VSTR = kBN + 4;         // LDS row stride of V^T (elements)
+    constexpr int VSTR = kBN + 8;         // LDS row stride of V^T (elements; 36 dwords)
     constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int KLD = (kBN * CPR) / kBlock;
 
@@ -279,9 +310,6 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     }
 
     const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
-    const uint16_t* Kc = (const uint16_t*)c.k + head_off;
-    const uint16_t* Vc = (const uint16_t*)c.v + head_off;
-    const uint16_t* Ks = (const uint16_t*)c.stage_k;
 
     // Key ranges in position space: 0 = prefix (cache), 1 = still-visible ring (cache),
     // 2 = the chunk (staged keys, input values).
@@ -289,7 +317,8 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     const int lo1 = n > P ? max(P, p_lo - W + 1) : n;
     const int lo2 = n, hi2 = p_hi + 1;
     const Walk wk{nA, lo1, n, lo2, hi2, P, p_lo - W + 1};
-    const TileSrc src{Kc, Vc, Ks, v_in, (size_t)b * chunk, n, P, W, c.Pmax, c.Hkv, h};
+    const TileSrc src{(const uint16_t*)c.k + head_off, (const uint16_t*)c.v + head_off,
+                      (const uint16_t*)c.stage_k, v_in, (size_t)b * chunk, n, P, W, c.Pmax, c.Hkv, h};
 
     u32x4 kreg[KLD], vreg[4];
     int seg = 0, t0 = -kBN;
@@ -326,6 +355,9 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
         }
 
         // ---- mask, online softmax -------------------------------------------------------
+        // Masked logits become -inf: exp2(-inf - m) is 0 for the finite running max m, which
+        // starts at kNeg and is only ever raised to a real tile maximum.
+        bf16x8 pb[2][PVS];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             if (!full) {
@@ -336,14 +368,15 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
                     for (int i = 0; i < 4; ++i) {
                         const int j = ct0 + kb * 16 + 4 * lg + i;
                         const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
-                        s[rb][kb][i] = vis ? s[rb][kb][i] : kNeg;
+                        s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
                     }
             }
-            float mt = s[rb][0][0];
+            float mt = fmaxf(s[rb][0][0], s[rb][0][1]);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[rb][kb][i]);
+                for (int i = (kb == 0 ? 2 : 0); i < 4; i += 2)
+                    mt = __builtin_fmaxf(__builtin_fmaxf(mt, s[rb][kb][i]), s[rb][kb][i + 1]);
             mt = row_max4(mt);
             const bool need = mt > m[rb] + kRescaleSlack;
             if (__any(need)) {
@@ -353,39 +386,31 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[rb][db] *= f;
             }
+            // probabilities -> bf16 B operands; their row sum from the same rounded values
             float acc = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int ps = 0; ps < PVS; ++ps) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float pr = __builtin_amdgcn_exp2f(s[rb][kb][i] - m[rb]);
-                    if (!full) pr = s[rb][kb][i] == kNeg ? 0.f : pr;
-                    s[rb][kb][i] = pr;
-                    acc += pr;
+                    pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i] - m[rb]);
+                    pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i] - m[rb]);
                 }
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    bf16x2 two = {pb[rb][ps][i], pb[rb][ps][i + 1]};
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, acc, false);
+                }
+            }
             lp[rb] += acc;
         }
 
         // ---- O^T += V^T P^T -------------------------------------------------------------
-        bf16x8 pb[2][PVS];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int ps = 0; ps < PVS; ++ps)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pb[rb][ps][i] = (__bf16)s[rb][2 * ps][i];
-                    pb[rb][ps][4 + i] = (__bf16)s[rb][2 * ps + 1][i];
-                }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int ps = 0; ps < PVS; ++ps) {
-                const uint16_t* vp = vt_s + (db * 16 + l16) * VSTR + ps * 32 + 4 * lg;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-                const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                const bf16x8 a = as_bf16x8(w);
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                    vt_s + (db * 16 + l16) * VSTR + ps * 32 + 8 * lg));
                 o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], o[0][db], 0, 0, 0);
                 o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], o[1][db], 0, 0, 0);
             }
