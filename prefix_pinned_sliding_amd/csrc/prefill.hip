@@ -358,6 +358,7 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
         // Masked logits become -inf: exp2(-inf - m) is 0 for the finite running max m, which
         // starts at kNeg and is only ever raised to a real tile maximum.
         bf16x8 pb[2][PVS];
+        float ml[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             if (!full) {
@@ -371,21 +372,29 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
                         s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
                     }
             }
-            float mt = fmaxf(s[rb][0][0], s[rb][0][1]);
+            ml[rb] = fmaxf(s[rb][0][0], s[rb][0][1]);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = (kb == 0 ? 2 : 0); i < 4; i += 2)
-                    mt = __builtin_fmaxf(__builtin_fmaxf(mt, s[rb][kb][i]), s[rb][kb][i + 1]);
-            mt = row_max4(mt);
-            const bool need = mt > m[rb] + kRescaleSlack;
-            if (__any(need)) {
+                    ml[rb] = __builtin_fmaxf(__builtin_fmaxf(ml[rb], s[rb][kb][i]), s[rb][kb][i + 1]);
+        }
+        // The running max of a row only moves when some lane's own max exceeds it by the
+        // slack; test that with one ballot and do the cross-lane row max only then.
+        if (__any(ml[0] > m[0] + kRescaleSlack || ml[1] > m[1] + kRescaleSlack)) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float mt = row_max4(ml[rb]);
+                const bool need = mt > m[rb] + kRescaleSlack;
                 const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
                 m[rb] = need ? mt : m[rb];
                 lp[rb] *= f;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[rb][db] *= f;
             }
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
             // probabilities -> bf16 B operands; their row sum from the same rounded values
             float acc = 0.f;
 #pragma unroll
