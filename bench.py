@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p100_w4096",
-                    choices=["decode_p100_w4096", "decode_p512_w16384", "ragged_decode"])
+                    choices=["decode_p100_w4096", "decode_p512_w16384", "ragged_decode",
+                             "decode_shared_p2000", "decode_private_p2000"])
     ap.add_argument("--t", type=int, default=0, help="override the start position t (flat-in-t sweeps)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -189,16 +190,26 @@ def main():
         wl = configs.decode_p100_w4096(t=args.t) if args.t else configs.decode_p100_w4096()
     elif args.workload == "decode_p512_w16384":
         wl = configs.decode_p512_w16384(t=args.t) if args.t else configs.decode_p512_w16384()
+    elif args.workload in ("decode_shared_p2000", "decode_private_p2000"):
+        wl = configs.decode_shared_p2000(t=args.t) if args.t else configs.decode_shared_p2000()
+        if args.workload == "decode_private_p2000":
+            wl.name = wl.name.replace("shared", "private")
     else:
         wl = configs.ragged_decode()
     B = wl.batch
     n0 = [t - 1 for t in wl.start]
     total = args.warmup + 2 * args.steps
     print(f"[bench] {wl.name}: filling {sum(n0)} tokens", file=sys.stderr, flush=True)
-    c = drive.make_cache(wl)
+    if args.workload == "decode_shared_p2000":
+        c = drive.make_cache(wl, n_shared=1, shared_max=wl.prefix[0], prefix_max=0)
+    else:
+        c = drive.make_cache(wl)
     if args.split_tokens:
         c.set_split_tokens(args.split_tokens)
-    drive.fill(c, wl, n0)
+    if args.workload in ("decode_shared_p2000", "decode_private_p2000"):
+        drive.fill_one_prompt(c, wl, n0, shared=args.workload == "decode_shared_p2000")
+    else:
+        drive.fill(c, wl, n0)
 
     # inputs of every step, resident before timing
     ks, vs, qs = [], [], []

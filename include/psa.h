@@ -78,6 +78,8 @@ typedef struct {
     int32_t max_chunk;   /* largest prefill chunk C (0: psa_prefill_attn unavailable) */
     double rope_base;    /* > 0, e.g. 10000 */
     float scale;         /* softmax scale; 0 selects 1 / sqrt(head_dim) */
+    int32_t n_shared_prefixes; /* >= 0: entries of the shared-prefix pool */
+    int32_t shared_prefix_max; /* >= 0: longest prefix one pool entry holds */
     int32_t reserved;    /* must be 0 */
 } psa_cache_desc;
 
@@ -85,10 +87,14 @@ typedef struct {
  * K and V: [B][H_kv][S][D] with S = prefix_max + window slots per (sequence, head):
  * slots [0, P_max) hold prefix positions p < P_b at slot p; slots [P_max, S) are the
  * ring, position p >= P_b at slot P_max + (p - P_b) mod W.
- * tags: [B][S] int32, the absolute position held by each slot, -1 if never written. */
+ * tags: [B][S] int32, the absolute position held by each slot, -1 if never written.
+ * pool K and V: [n_shared_prefixes][H_kv][shared_prefix_max][D], position p of entry e
+ * at row p (absent when n_shared_prefixes is 0). */
 typedef struct {
     size_t k_offset;
     size_t v_offset;
+    size_t pool_k_offset;
+    size_t pool_v_offset;
     size_t tags_offset;
     size_t state_offset;  /* library-private per-sequence state */
     size_t work_offset;   /* library-private workspace */
@@ -122,6 +128,26 @@ int psa_cache_destroy(psa_cache *cache);
  * appended afterwards ([PS] 03: the prefix KV is encoded once and never evicted). */
 int psa_seq_reset(psa_cache *cache, int32_t seq, int32_t prefix_len, psa_stream stream);
 
+/* Shared pinned prefixes ([KV-Lean] 6.1-6.2: a logical cache read through a table of
+ * physical blocks; a prompt's prefix reused across requests is safe when its positions
+ * are the same, which Continue PE guarantees: prefix tokens sit at positions 0 .. P-1
+ * in every sequence). One pool entry holds the K/V of one prompt prefix; any number of
+ * sequences (e.g. many sampled runs of one problem) read it instead of holding a copy.
+ *
+ * psa_prefix_load: write pool entry `prefix_id` with `len` tokens at positions 0 .. len-1
+ * (0 <= len <= shared_prefix_max; keys rotated at their positions and rounded as in
+ * psa_append). k, v: [len][H_kv][D]. Errors: PSA_ERR_ARG for an out-of-range id or
+ * length; PSA_ERR_STATE while sequences are attached to the entry. */
+int psa_prefix_load(psa_cache *cache, int32_t prefix_id, int32_t len, const void *k, const void *v,
+                    psa_stream stream);
+
+/* Start (or restart) sequence `seq` on pool entry `prefix_id`: its pinned prefix is that
+ * entry (P_b = the entry's length) and its history already holds positions 0 .. P_b - 1;
+ * the next append is position P_b. The sequence reads the prefix from the pool and never
+ * writes it. psa_seq_reset detaches. Errors: PSA_ERR_STATE if the entry was never
+ * loaded; PSA_ERR_ARG for an out-of-range id. */
+int psa_seq_attach(psa_cache *cache, int32_t seq, int32_t prefix_id, psa_stream stream);
+
 /* Append new tokens to every sequence ([PS] 03 generation loop; [KV-Lean] 2.2, 3.3:
  * append at the tail, evict the oldest once the window holds more than W).
  * k, v: [B][n_stride][H_kv][D]. Sequence b appends n_b tokens, rows 0 .. n_b - 1 of
@@ -153,9 +179,11 @@ int psa_prefill_attn(psa_cache *cache, int32_t chunk, const void *q, const void 
                      const void *v, void *out, float *lse, psa_stream stream);
 
 /* Copy sequence `seq`'s logical cache to host memory ([KV-Lean] 3.4 ring read back
- * as a list; 6.3 export and compare against the list model): the prefix entries,
- * then the window oldest first, count = min(len, P_b + W) entries. k_host, v_host:
- * [S][H_kv][D] (S = prefix_max + window entries of capacity), pos_host: [S] int32
+ * as a list; 6.3 export and compare against the list model): the prefix entries (from
+ * the pool for an attached sequence), then the window oldest first,
+ * count = min(len, P_b + W) entries. k_host, v_host:
+ * [S][H_kv][D] (capacity S = max(prefix_max, shared_prefix_max) + window entries),
+ * pos_host: [S] int32
  * absolute positions; any of the three may be NULL. Waits for `stream`. */
 int psa_export(psa_cache *cache, int32_t seq, void *k_host, void *v_host, int32_t *pos_host,
                int32_t *count, psa_stream stream);

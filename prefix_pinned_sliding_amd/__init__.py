@@ -38,6 +38,8 @@ class Desc(ctypes.Structure):
         ("max_chunk", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
         ("scale", ctypes.c_float),
+        ("n_shared_prefixes", ctypes.c_int32),
+        ("shared_prefix_max", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -47,6 +49,8 @@ class Layout(ctypes.Structure):
     _fields_ = [
         ("k_offset", ctypes.c_size_t),
         ("v_offset", ctypes.c_size_t),
+        ("pool_k_offset", ctypes.c_size_t),
+        ("pool_v_offset", ctypes.c_size_t),
         ("tags_offset", ctypes.c_size_t),
         ("state_offset", ctypes.c_size_t),
         ("work_offset", ctypes.c_size_t),
@@ -68,6 +72,8 @@ def _load() -> ctypes.CDLL:
         "psa_cache_create": (ctypes.c_int, [ctypes.POINTER(Desc), P, SZ, P, ctypes.POINTER(P)]),
         "psa_cache_destroy": (ctypes.c_int, [P]),
         "psa_seq_reset": (ctypes.c_int, [P, I32, I32, P]),
+        "psa_prefix_load": (ctypes.c_int, [P, I32, I32, P, P, P]),
+        "psa_seq_attach": (ctypes.c_int, [P, I32, I32, P]),
         "psa_append": (ctypes.c_int, [P, P, I32, P, P, I32, P]),
         "psa_decode_attn": (ctypes.c_int, [P, P, P, P, P]),
         "psa_prefill_attn": (ctypes.c_int, [P, I32, P, P, P, P, P, P]),
@@ -108,11 +114,12 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def make_desc(max_batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, prefix_max: int,
               window: int, dtype: torch.dtype = torch.bfloat16, rope_base: float = 10000.0,
-              scale: float = 0.0, max_chunk: int = 0) -> Desc:
+              scale: float = 0.0, max_chunk: int = 0, n_shared_prefixes: int = 0,
+              shared_prefix_max: int = 0) -> Desc:
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {dtype}")
     return Desc(max_batch, n_q_heads, n_kv_heads, head_dim, prefix_max, window, _DTYPES[dtype],
-                max_chunk, float(rope_base), float(scale), 0)
+                max_chunk, float(rope_base), float(scale), n_shared_prefixes, shared_prefix_max, 0)
 
 
 def cache_bytes(desc: Desc) -> int:
@@ -140,9 +147,11 @@ class Cache:
     def __init__(self, max_batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  prefix_max: int, window: int, dtype: torch.dtype = torch.bfloat16,
                  rope_base: float = 10000.0, scale: float = 0.0, max_chunk: int = 0,
-                 device=None, stream=None):
+                 device=None, stream=None, n_shared_prefixes: int = 0, shared_prefix_max: int = 0):
         self.desc = make_desc(max_batch, n_q_heads, n_kv_heads, head_dim, prefix_max, window,
-                              dtype, rope_base, scale, max_chunk)
+                              dtype, rope_base, scale, max_chunk, n_shared_prefixes,
+                              shared_prefix_max)
+        self.n_shared, self.shared_max = n_shared_prefixes, shared_prefix_max
         self.dtype = dtype
         self.B, self.Hq, self.Hkv, self.D = max_batch, n_q_heads, n_kv_heads, head_dim
         self.P_max, self.W, self.max_chunk = prefix_max, window, max_chunk
@@ -182,6 +191,21 @@ class Cache:
     # -- calls ---------------------------------------------------------------------------
     def reset(self, seq: int, prefix_len: int, stream=None) -> None:
         _check(lib.psa_seq_reset(self._h, seq, prefix_len, _stream(stream)), "psa_seq_reset")
+
+    def prefix_load(self, prefix_id: int, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        """Write shared-prefix entry `prefix_id`: k, v [len][H_kv][D] at positions 0 .. len-1."""
+        for name, t in (("k", k), ("v", v)):
+            if t.dtype != self.dtype or not t.is_contiguous() or t.dim() != 3 or \
+                    tuple(t.shape[1:]) != (self.Hkv, self.D):
+                raise ValueError(f"{name} must be a contiguous {self.dtype} [len][{self.Hkv}][{self.D}] tensor")
+        if k.shape[0] != v.shape[0]:
+            raise ValueError("k and v differ in length")
+        _check(lib.psa_prefix_load(self._h, prefix_id, k.shape[0], _ptr(k), _ptr(v), _stream(stream)),
+               "psa_prefix_load")
+
+    def attach(self, seq: int, prefix_id: int, stream=None) -> None:
+        """Start sequence `seq` on shared-prefix entry `prefix_id`."""
+        _check(lib.psa_seq_attach(self._h, seq, prefix_id, _stream(stream)), "psa_seq_attach")
 
     def _kv_check(self, t: torch.Tensor, name: str, heads: int) -> int:
         if t.dtype != self.dtype or not t.is_contiguous() or t.device.type != "cuda":
@@ -237,7 +261,7 @@ class Cache:
 
     def export(self, seq: int, stream=None):
         """Logical view of one sequence on the host: (k [n][H_kv][D], v, positions [n])."""
-        cap = self.P_max + self.W
+        cap = max(self.P_max, self.shared_max) + self.W
         k = torch.empty((cap, self.Hkv, self.D), dtype=self.dtype)
         v = torch.empty_like(k)
         pos = torch.empty(cap, dtype=torch.int32)

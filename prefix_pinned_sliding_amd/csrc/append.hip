@@ -25,20 +25,52 @@ __device__ __forceinline__ double to_f64(float f) { return (double)f; }
 __device__ __forceinline__ uint16_t store_as(double x, uint16_t*) { return f64_to_bf16_bits(x); }
 __device__ __forceinline__ float store_as(double x, float*) { return (float)x; }
 
-__global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_state) {
+// Tags -1; lengths, prefix lengths and token counts 0; prefix entries -1 (own prefix).
+__global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_zero,
+                            int32_t* pid, int B) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_tags) tags[i] = -1;
-    if (i < (size_t)n_state) state[i] = 0;
+    if (i < (size_t)n_zero) state[i] = 0;
+    if (i < (size_t)B) pid[i] = -1;
 }
 
-__global__ void seq_reset_kernel(int32_t* tags, int S, int32_t* len_cur, int32_t* pre, int seq,
-                                 int prefix_len) {
+__global__ void seq_reset_kernel(int32_t* tags, int S, int32_t* len_cur, int32_t* pre,
+                                 int32_t* pid, int seq, int prefix_len, int len0, int prefix_id) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < S) tags[(size_t)seq * S + i] = -1;
     if (i == 0) {
-        len_cur[seq] = 0;
+        len_cur[seq] = len0;
         pre[seq] = prefix_len;
+        pid[seq] = prefix_id;
     }
+}
+
+// One thread per (token j, KV head h, pair i) of a shared prefix: position p = j, stored
+// exactly as psa_append stores a prefix token (rotated at p, rounded once).
+template <int DT, int D>
+__global__ __launch_bounds__(kBlock) void pool_load_kernel(DevCache c, int id, int len,
+                                                           const typename Elem<DT>::T* k,
+                                                           const typename Elem<DT>::T* v) {
+    using T = typename Elem<DT>::T;
+    constexpr int H = D / 2;
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t total = (size_t)len * c.Hkv * H;
+    if (idx >= total) return;
+    const int i = (int)(idx % H);
+    const size_t r = idx / H;
+    const int h = (int)(r % c.Hkv);
+    const int j = (int)(r / c.Hkv);
+    const size_t src = ((size_t)j * c.Hkv + h) * D;
+    const size_t dst = (((size_t)id * c.Hkv + h) * c.shared_max + j) * D;
+    double sn, cs, xr, yr;
+    angle_sincos(j, c.inv_freq[i], &sn, &cs);
+    rotate_with(to_f64(k[src + i]), to_f64(k[src + i + H]), sn, cs, &xr, &yr);
+    T* K = (T*)c.pool_k;
+    T* V = (T*)c.pool_v;
+    K[dst + i] = store_as(xr, (T*)nullptr);
+    K[dst + i + H] = store_as(yr, (T*)nullptr);
+    V[dst + i] = v[src + i];
+    V[dst + i + H] = v[src + i + H];
 }
 
 // One thread per (sequence b, token j, KV head h, rotation pair i): a one-token append is
@@ -104,16 +136,34 @@ inline unsigned blocks_for(size_t n) { return (unsigned)((n + kBlock - 1) / kBlo
 
 hipError_t launch_init(const DevCache& c, hipStream_t s) {
     const size_t n_tags = (size_t)c.B * c.S;
-    const int n_state = 4 * c.B;   // len[0], len[1], pre, nnew are contiguous
-    const size_t n = n_tags > (size_t)n_state ? n_tags : (size_t)n_state;
+    const int n_zero = 4 * c.B;   // len[0], len[1], pre, nnew are contiguous
+    const size_t n = n_tags > (size_t)n_zero ? n_tags : (size_t)n_zero;
     hipLaunchKernelGGL(init_kernel, dim3(blocks_for(n)), dim3(kBlock), 0, s, c.tags, n_tags,
-                       c.len[0], n_state);
+                       c.len[0], n_zero, c.pid, c.B);
     return hipGetLastError();
 }
 
-hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int cur, hipStream_t s) {
+hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int len0, int pid, int cur,
+                            hipStream_t s) {
     hipLaunchKernelGGL(seq_reset_kernel, dim3(blocks_for((size_t)c.S)), dim3(kBlock), 0, s, c.tags,
-                       c.S, c.len[cur], c.pre, seq, prefix_len);
+                       c.S, c.len[cur], c.pre, c.pid, seq, prefix_len, len0, pid);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_load(const DevCache& c, int id, int len, const void* k, const void* v,
+                            hipStream_t s) {
+    const size_t total = (size_t)len * c.Hkv * (c.D / 2);
+    if (total == 0) return hipSuccess;
+    const dim3 grid(blocks_for(total));
+#define PSA_POOL(DT, DD)                                                                   \
+    hipLaunchKernelGGL((pool_load_kernel<DT, DD>), grid, dim3(kBlock), 0, s, c, id, len, \
+                       (const typename Elem<DT>::T*)k, (const typename Elem<DT>::T*)v)
+    if (c.dtype == PSA_BF16) {
+        if (c.D == 128) PSA_POOL(PSA_BF16, 128); else PSA_POOL(PSA_BF16, 64);
+    } else {
+        if (c.D == 128) PSA_POOL(PSA_F32, 128); else PSA_POOL(PSA_F32, 64);
+    }
+#undef PSA_POOL
     return hipGetLastError();
 }
 

@@ -161,18 +161,25 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     __shared__ float red_l[kWaves][ROWS][G];
     __shared__ float red_m[kWaves][G];
 
+    // Prefix rows: the sequence's own slots, or its shared-prefix pool entry; ring rows
+    // follow the own prefix slots.
     const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
-    const T* Kb = (const T*)c.k + head_off;
-    const T* Vb = (const T*)c.v + head_off;
+    const int pid = c.pid[b];
+    const size_t pre_off = pid >= 0 ? ((size_t)pid * c.Hkv + h) * (size_t)c.shared_max * D : head_off;
+    const T* Kp = (const T*)(pid >= 0 ? c.pool_k : c.k) + pre_off;
+    const T* Vp = (const T*)(pid >= 0 ? c.pool_v : c.v) + pre_off;
+    const T* Kr = (const T*)c.k + head_off + (size_t)c.Pmax * D;
+    const T* Vr = (const T*)c.v + head_off + (size_t)c.Pmax * D;
 
-    // Logical entry i -> physical slot: the prefix rows, then the filled ring rows.
+    // Logical entry i -> physical row: the prefix rows, then the filled ring rows.
     auto load = [&](Tile& t, int base_i) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = min(base_i + u * KPW + grp, i1 - 1);
-            const int slot = i < n_pre ? i : c.Pmax + (i - n_pre);
-            const u32x4* kp = reinterpret_cast<const u32x4*>(Kb + (size_t)slot * D);
-            const u32x4* vp = reinterpret_cast<const u32x4*>(Vb + (size_t)slot * D);
+            const bool pre = i < n_pre;
+            const size_t row = (size_t)(pre ? i : i - n_pre) * D;
+            const u32x4* kp = reinterpret_cast<const u32x4*>((pre ? Kp : Kr) + row);
+            const u32x4* vp = reinterpret_cast<const u32x4*>((pre ? Vp : Vr) + row);
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 t.k[u][cc] = __builtin_nontemporal_load(kp + cc * LPK + sub);

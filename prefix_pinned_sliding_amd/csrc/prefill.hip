@@ -147,6 +147,7 @@ __device__ __forceinline__ bool walk_next(const Walk& w, int& seg, int& t0) {
 // Where the K and V rows of position j live for key range `seg`.
 struct TileSrc {
     const uint16_t *k_cache, *v_cache, *k_chunk, *v_chunk;
+    const uint16_t *k_prefix, *v_prefix;   // own prefix slots or the shared-prefix entry
     size_t chunk_row0;   // b * chunk
     int n, P, W, Pmax, Hkv, h;
 };
@@ -176,8 +177,8 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
         stride = D;
         ring0 = (t0 - s.P) % s.W;
     } else {
-        kb = s.k_cache + (size_t)t0 * D;
-        vb = s.v_cache + (size_t)t0 * D;
+        kb = s.k_prefix + (size_t)t0 * D;
+        vb = s.v_prefix + (size_t)t0 * D;
         stride = D;
     }
     auto row = [&](int off) -> int {   // row index relative to the tile's base pointer
@@ -317,8 +318,13 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     const int lo1 = n > P ? max(P, p_lo - W + 1) : n;
     const int lo2 = n, hi2 = p_hi + 1;
     const Walk wk{nA, lo1, n, lo2, hi2, P, p_lo - W + 1};
+    const int pid = c.pid[b];
+    const size_t pre_off = pid >= 0 ? ((size_t)pid * c.Hkv + h) * (size_t)c.shared_max * D : head_off;
     const TileSrc src{(const uint16_t*)c.k + head_off, (const uint16_t*)c.v + head_off,
-                      (const uint16_t*)c.stage_k, v_in, (size_t)b * chunk, n, P, W, c.Pmax, c.Hkv, h};
+                      (const uint16_t*)c.stage_k, v_in,
+                      (const uint16_t*)(pid >= 0 ? c.pool_k : c.k) + pre_off,
+                      (const uint16_t*)(pid >= 0 ? c.pool_v : c.v) + pre_off,
+                      (size_t)b * chunk, n, P, W, c.Pmax, c.Hkv, h};
 
     u32x4 kreg[KLD], vreg[4];
     int seg = 0, t0 = -kBN;

@@ -40,6 +40,9 @@ struct psa_cache {
     int cur;                       // which device length buffer is current
     std::vector<int64_t> len;      // host mirror of history lengths
     std::vector<int32_t> pre;      // host mirror of P_b; -1 = never reset
+    std::vector<int32_t> pid;      // shared-prefix entry per sequence, -1 = own prefix
+    std::vector<int32_t> pool_len; // tokens held by each pool entry, -1 = never loaded
+    std::vector<int32_t> attached; // sequences attached to each pool entry
     int32_t split_tokens;          // 0 = automatic
     int resident_wgs;              // decode workgroups resident at once (0 = not yet queried)
     bool profiling;
@@ -68,6 +71,11 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     if (d.max_chunk < 0) return bad("max_chunk must be >= 0");
     if (!(d.rope_base > 0.0) || !isfinite(d.rope_base)) return bad("rope_base must be finite and > 0");
     if (!(d.scale >= 0.f) || !isfinite(d.scale)) return bad("scale must be finite and >= 0");
+    if (d.n_shared_prefixes < 0 || d.shared_prefix_max < 0)
+        return bad("n_shared_prefixes and shared_prefix_max must be >= 0");
+    if (d.n_shared_prefixes > 0 && d.shared_prefix_max < 1)
+        return bad("shared_prefix_max must be >= 1 when the pool has entries");
+    if ((int64_t)d.shared_prefix_max + d.window > (1 << 30)) return bad("shared_prefix_max too large");
     if (d.reserved != 0) return bad("reserved must be 0");
     const int64_t S = (int64_t)d.prefix_max + d.window;
     if (S > (1 << 30)) return bad("prefix_max + window too large");
@@ -79,8 +87,11 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     size_t off = 0;
     L->k = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
     L->v = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
+    const size_t pool = (size_t)d.n_shared_prefixes * Hkv * (size_t)d.shared_prefix_max * D * elem;
+    L->pool_k = off;   off = align_up(off + pool, A);
+    L->pool_v = off;   off = align_up(off + pool, A);
     L->tags = off;     off = align_up(off + B * (size_t)S * 4, A);
-    L->state = off;    off = align_up(off + 4 * B * 4, A);
+    L->state = off;    off = align_up(off + 5 * B * 4, A);
     L->inv_freq = off; off = align_up(off + D / 2 * 8, A);
     L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
     L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
@@ -176,6 +187,8 @@ PSA_API int psa_cache_layout(const psa_cache_desc* desc, psa_layout* out) {
     if (!psa::compute_layout(*desc, &L, &why)) return fail(PSA_ERR_ARG, why);
     out->k_offset = L.k;
     out->v_offset = L.v;
+    out->pool_k_offset = L.pool_k;
+    out->pool_v_offset = L.pool_v;
     out->tags_offset = L.tags;
     out->state_offset = L.state;
     out->work_offset = L.inv_freq;
@@ -207,6 +220,9 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     c->cur = 0;
     c->len.assign(desc->max_batch, 0);
     c->pre.assign(desc->max_batch, -1);
+    c->pid.assign(desc->max_batch, -1);
+    c->pool_len.assign(desc->n_shared_prefixes, -1);
+    c->attached.assign(desc->n_shared_prefixes, 0);
     c->split_tokens = 0;
     c->resident_wgs = 0;
     c->profiling = false;
@@ -218,12 +234,15 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     psa::DevCache& d = c->dev;
     d.k = base + L.k;
     d.v = base + L.v;
+    d.pool_k = base + L.pool_k;
+    d.pool_v = base + L.pool_v;
     d.tags = (int32_t*)(base + L.tags);
     int32_t* st = (int32_t*)(base + L.state);
     d.len[0] = st;
     d.len[1] = st + desc->max_batch;
     d.pre = st + 2 * desc->max_batch;
     d.nnew = st + 3 * desc->max_batch;
+    d.pid = st + 4 * desc->max_batch;
     d.inv_freq = (double*)(base + L.inv_freq);
     d.part_o = (float*)(base + L.part_o);
     d.part_ml = (float*)(base + L.part_ml);
@@ -239,6 +258,8 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.dtype = desc->dtype;
     d.max_chunk = desc->max_chunk;
     d.max_splits = L.max_splits;
+    d.n_shared = desc->n_shared_prefixes;
+    d.shared_max = desc->shared_prefix_max;
     d.scale = desc->scale > 0.f ? desc->scale : (float)(1.0 / sqrt((double)desc->head_dim));
 
     // theta_i = base^(-2i/D) in float64 on the host.
@@ -268,15 +289,60 @@ PSA_API int psa_cache_destroy(psa_cache* c) {
     return PSA_OK;
 }
 
+namespace {
+
+void detach(psa_cache* c, int32_t seq) {
+    if (c->pid[seq] >= 0) c->attached[c->pid[seq]] -= 1;
+    c->pid[seq] = -1;
+}
+
+}  // namespace
+
 PSA_API int psa_seq_reset(psa_cache* c, int32_t seq, int32_t prefix_len, psa_stream stream) {
     if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
     if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
     if (prefix_len < 0 || prefix_len > c->desc.prefix_max)
         return fail(PSA_ERR_ARG, "prefix_len must be in [0, prefix_max]");
-    const hipError_t e = psa::launch_seq_reset(c->dev, seq, prefix_len, c->cur, (hipStream_t)stream);
+    const hipError_t e =
+        psa::launch_seq_reset(c->dev, seq, prefix_len, 0, -1, c->cur, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sequence reset");
+    detach(c, seq);
     c->len[seq] = 0;
     c->pre[seq] = prefix_len;
+    return PSA_OK;
+}
+
+PSA_API int psa_prefix_load(psa_cache* c, int32_t prefix_id, int32_t len, const void* k,
+                            const void* v, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (prefix_id < 0 || prefix_id >= c->desc.n_shared_prefixes)
+        return fail(PSA_ERR_ARG, "prefix_id out of range");
+    if (len < 0 || len > c->desc.shared_prefix_max)
+        return fail(PSA_ERR_ARG, "len must be in [0, shared_prefix_max]");
+    if (len > 0 && (k == nullptr || v == nullptr)) return fail(PSA_ERR_ARG, "k or v is NULL");
+    if (c->attached[prefix_id] > 0)
+        return fail(PSA_ERR_STATE, "pool entry has attached sequences");
+    const hipError_t e = psa::launch_pool_load(c->dev, prefix_id, len, k, v, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefix load");
+    c->pool_len[prefix_id] = len;
+    return PSA_OK;
+}
+
+PSA_API int psa_seq_attach(psa_cache* c, int32_t seq, int32_t prefix_id, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    if (prefix_id < 0 || prefix_id >= c->desc.n_shared_prefixes)
+        return fail(PSA_ERR_ARG, "prefix_id out of range");
+    const int32_t P = c->pool_len[prefix_id];
+    if (P < 0) return fail(PSA_ERR_STATE, "pool entry was never loaded");
+    const hipError_t e =
+        psa::launch_seq_reset(c->dev, seq, P, P, prefix_id, c->cur, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sequence attach");
+    detach(c, seq);
+    c->pid[seq] = prefix_id;
+    c->attached[prefix_id] += 1;
+    c->len[seq] = P;
+    c->pre[seq] = P;
     return PSA_OK;
 }
 
@@ -398,16 +464,41 @@ PSA_API int psa_export(psa_cache* c, int32_t seq, void* k_host, void* v_host, in
     if (e == hipSuccess)
         e = hipMemcpyAsync(tags.data(), d.tags + (size_t)seq * S, S * sizeof(int32_t),
                            hipMemcpyDeviceToHost, s);
+    // An attached sequence's prefix rows live in its pool entry (positions 0 .. P_b - 1).
+    const int32_t pid = c->pid[seq];
+    const size_t SP = (size_t)d.shared_max;
+    std::vector<char> pk, pv;
+    if (pid >= 0 && n_pre > 0) {
+        const size_t pool_bytes = Hkv * SP * row, at = (size_t)pid * pool_bytes;
+        if (e == hipSuccess && k_host) {
+            pk.resize(pool_bytes);
+            e = hipMemcpyAsync(pk.data(), (const char*)d.pool_k + at, pool_bytes,
+                               hipMemcpyDeviceToHost, s);
+        }
+        if (e == hipSuccess && v_host) {
+            pv.resize(pool_bytes);
+            e = hipMemcpyAsync(pv.data(), (const char*)d.pool_v + at, pool_bytes,
+                               hipMemcpyDeviceToHost, s);
+        }
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "export copy");
     // Logical order: prefix slots, then the ring from the oldest entry ([KV-Lean] 3.4).
     for (int64_t i = 0; i < cnt; ++i) {
+        const bool pool_row = pid >= 0 && i < n_pre;
         const size_t slot = i < n_pre ? (size_t)i : (size_t)(d.Pmax + (head + (i - n_pre)) % W);
-        if (pos_host) pos_host[i] = tags[slot];
+        if (pos_host) pos_host[i] = pool_row ? (int32_t)i : tags[slot];
         for (size_t h = 0; h < Hkv; ++h) {
-            const size_t from = (h * S + slot) * row, to = ((size_t)i * Hkv + h) * row;
-            if (k_host) memcpy((char*)k_host + to, kbuf.data() + from, row);
-            if (v_host) memcpy((char*)v_host + to, vbuf.data() + from, row);
+            const size_t to = ((size_t)i * Hkv + h) * row;
+            if (pool_row) {
+                const size_t from = (h * SP + (size_t)i) * row;
+                if (k_host) memcpy((char*)k_host + to, pk.data() + from, row);
+                if (v_host) memcpy((char*)v_host + to, pv.data() + from, row);
+            } else {
+                const size_t from = (h * S + slot) * row;
+                if (k_host) memcpy((char*)k_host + to, kbuf.data() + from, row);
+                if (v_host) memcpy((char*)v_host + to, vbuf.data() + from, row);
+            }
         }
     }
     *count = (int32_t)cnt;

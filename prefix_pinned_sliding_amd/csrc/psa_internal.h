@@ -16,21 +16,24 @@ constexpr int kMaxGroup = 8;         // largest supported H_q / H_kv
 struct DevCache {
     void* k;             // [B][Hkv][S][D] storage dtype
     void* v;             // [B][Hkv][S][D]
+    void* pool_k;        // [n_shared][Hkv][shared_max][D] shared prefixes
+    void* pool_v;
     int32_t* tags;       // [B][S]
     int32_t* len[2];     // [B] history lengths; len[cur] is current, the other is written by append
     int32_t* pre;        // [B] prefix length P_b
     int32_t* nnew;       // [B] per-call token counts (ragged append)
+    int32_t* pid;        // [B] shared-prefix entry of each sequence, -1 for its own prefix
     double* inv_freq;    // [D/2] theta_i
     float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
     void* stage_k;       // [B][max_chunk][Hkv][D] rotated prefill-chunk keys (stored bytes)
     void* stage_q;       // [B][max_chunk][Hq][D] rotated, scaled prefill-chunk queries (bf16)
-    int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits;
+    int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits, n_shared, shared_max;
     float scale;
 };
 
 struct Layout {
-    size_t k, v, tags, state, inv_freq, part_o, part_ml, stage_k, stage_q, total;
+    size_t k, v, pool_k, pool_v, tags, state, inv_freq, part_o, part_ml, stage_k, stage_q, total;
     int32_t S, elem, max_splits;
 };
 
@@ -38,7 +41,12 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why);
 
 // Kernel launchers (stream-ordered, asynchronous). They return the launch status.
 hipError_t launch_init(const DevCache& c, hipStream_t s);
-hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int cur, hipStream_t s);
+// Start a sequence: tags -1, length `len0`, prefix length `prefix_len`, prefix entry `pid`.
+hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int len0, int pid, int cur,
+                            hipStream_t s);
+// Rotate and store `len` prefix tokens (k, v: [len][Hkv][D]) into pool entry `id`.
+hipError_t launch_pool_load(const DevCache& c, int id, int len, const void* k, const void* v,
+                            hipStream_t s);
 // Append n tokens per sequence (n_uniform, or nnew[] on device when ragged != 0).
 // k/v: [B][n_stride][Hkv][D]; k_rotated != 0 means k already holds rotated, rounded keys.
 hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_stride,

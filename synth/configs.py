@@ -84,12 +84,20 @@ def ragged_decode(seed: int = 0, batch: int = 256, steps: int = 64) -> Workload:
                     4096, prefix, starts, "decode", steps=steps, seed=seed)
 
 
+def decode_shared_p2000(seed: int = 0, batch: int = 64, t: int = 32768) -> Workload:
+    """bf16, 64 runs of one prompt: a 2000-token prefix (sequence 0's values for every run),
+    W=4096, t=32768, 16/8 heads, D=128. Used with the prefix shared or copied per run."""
+    return Workload(f"decode-bf16-B{batch}-P2000shared-W4096-t{t}", torch.bfloat16, batch, 16, 8,
+                    128, 4096, [2000] * batch, [t] * batch, "decode", steps=1, seed=seed)
+
+
 ALL = {
     "tiny_fp32": tiny_fp32,
     "decode_p100_w4096": decode_p100_w4096,
     "prefill_chunk512": prefill_chunk512,
     "decode_p512_w16384": decode_p512_w16384,
     "ragged_decode": ragged_decode,
+    "decode_shared_p2000": decode_shared_p2000,
 }
 
 
