@@ -41,6 +41,8 @@ def parse():
                              "decode_shared_p2000", "decode_private_p2000"])
     ap.add_argument("--t", type=int, default=0, help="override the start position t (flat-in-t sweeps)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--pe", default="continue", choices=["continue", "reset"],
+                    help="position encoding of attended tokens (reset: renumber the cache list)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
@@ -201,9 +203,9 @@ def main():
     total = args.warmup + 2 * args.steps
     print(f"[bench] {wl.name}: filling {sum(n0)} tokens", file=sys.stderr, flush=True)
     if args.workload == "decode_shared_p2000":
-        c = drive.make_cache(wl, n_shared=1, shared_max=wl.prefix[0], prefix_max=0)
+        c = drive.make_cache(wl, n_shared=1, shared_max=wl.prefix[0], prefix_max=0, pe=args.pe)
     else:
-        c = drive.make_cache(wl)
+        c = drive.make_cache(wl, pe=args.pe)
     if args.split_tokens:
         c.set_split_tokens(args.split_tokens)
     if args.workload in ("decode_shared_p2000", "decode_private_p2000"):
@@ -277,7 +279,8 @@ def main():
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
                    "prefix": wl.prefix[0] if len(set(wl.prefix)) == 1 else "ragged",
                    "window": wl.window, "t": wl.start[0] if len(set(wl.start)) == 1 else "ragged",
-                   "visible_tokens_per_step": vis, "parallelism": "single GPU"},
+                   "visible_tokens_per_step": vis, "parallelism": "single GPU",
+                   "position_encoding": args.pe},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel": "decode_partial",

@@ -80,8 +80,20 @@ typedef struct {
     float scale;         /* softmax scale; 0 selects 1 / sqrt(head_dim) */
     int32_t n_shared_prefixes; /* >= 0: entries of the shared-prefix pool */
     int32_t shared_prefix_max; /* >= 0: longest prefix one pool entry holds */
+    int32_t pe_mode;     /* PSA_PE_CONTINUE or PSA_PE_RESET */
     int32_t reserved;    /* must be 0 */
 } psa_cache_desc;
+
+/* Position encoding of attended tokens ([PS] 05).
+ * CONTINUE: every token keeps its absolute position (the method's choice).
+ * RESET: the attended tokens are renumbered as one sequence, prefix first: prefix token j
+ *   keeps j, window token j gets P_b + (j - base) with base the oldest window position,
+ *   and the query the position of the newest window entry. Stored keys are the same in
+ *   both modes (rotated at absolute positions); with rotary encoding only position
+ *   differences matter, and renumbering changes only the query-to-prefix distances, so
+ *   RESET rotates the query at its renumbered position for prefix keys and at its
+ *   absolute position for window keys. */
+enum { PSA_PE_CONTINUE = 0, PSA_PE_RESET = 1 };
 
 /* Byte offsets of the regions the library carves out of the caller's device buffer.
  * K and V: [B][H_kv][S][D] with S = prefix_max + window slots per (sequence, head):

@@ -54,8 +54,25 @@ def _softmax_attend(logits: np.ndarray, vals: np.ndarray, rows=None) -> Tuple[np
     return (wv @ vals) / l, float(m + np.log(l))
 
 
+def reset_positions(P: int, W: int, p: int, keys: np.ndarray) -> Tuple[int, np.ndarray]:
+    """Positions under Reset PE ([PS] 05): the attended tokens are renumbered as one
+    contiguous sequence, prefix first, window after it.
+
+    The reading taken here: the model sees the cache list [prefix, window] as positions
+    0 .. len - 1, so prefix token j keeps position j and window token j (absolute) gets
+    P + (j - base) with base = max(P, p - W + 1) the oldest window position; the query
+    (the newest window token) gets P + (p - base). Inside the prefix (p < P) nothing
+    moves. Returns (query position, key positions).
+    """
+    keys = np.asarray(keys, dtype=np.int64)
+    if p < P:
+        return p, keys
+    base = max(P, p - W + 1)
+    return P + (p - base), np.where(keys < P, keys, P + (keys - base))
+
+
 def decode_query(q: np.ndarray, p: int, hist: History, P: int, W: int, n_kv_heads: int,
-                 base: float, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+                 base: float, scale: float, pe: str = "continue") -> Tuple[np.ndarray, np.ndarray]:
     """Attention of one token's queries q[H_q, D] at absolute position p.
 
     Builds the length-(p+1) logit vector of every query head, -inf where the
@@ -63,6 +80,9 @@ def decode_query(q: np.ndarray, p: int, hist: History, P: int, W: int, n_kv_head
     visible keys and values are fetched from `hist`: a masked logit is -inf
     whatever its key holds. Query head hq reads KV head hq // (H_q / H_kv)
     (contiguous groups; the pages do not discuss grouped-query heads).
+
+    `pe` = "continue" rotates every token at its absolute position ([PS] 05, the method's
+    choice); "reset" rotates at the positions of `reset_positions`.
 
     Returns (out[H_q, D], lse[H_q]) in float64; lse is the natural-log
     log-sum-exp of the scaled logits.
@@ -73,8 +93,9 @@ def decode_query(q: np.ndarray, p: int, hist: History, P: int, W: int, n_kv_head
     mask = visible_mask(P, W, p)
     pos = np.nonzero(mask)[0]
     k, v = hist(pos)
-    qr = rope.rotate(q, np.full(Hq, p), base)
-    kr = rope.rotate(k, np.broadcast_to(pos[:, None], k.shape[:2]), base)
+    qpos, kpos = (p, pos) if pe == "continue" else reset_positions(P, W, p, pos)
+    qr = rope.rotate(q, np.full(Hq, qpos), base)
+    kr = rope.rotate(k, np.broadcast_to(kpos[:, None], k.shape[:2]), base)
     out = np.empty((Hq, D))
     lse = np.empty(Hq)
     for hq in range(Hq):
@@ -124,7 +145,8 @@ def decode_batch(q: np.ndarray, positions, hists, prefixes, W: int, n_kv_heads: 
 
 
 def prefill_chunk(q: np.ndarray, n: int, hist: History, P: int, W: int, n_kv_heads: int,
-                  base: float, scale: float, rows=None) -> Tuple[np.ndarray, np.ndarray]:
+                  base: float, scale: float, rows=None, pe: str = "continue"
+                  ) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of a chunk of queries q[C, H_q, D] at positions n .. n + C - 1.
 
     Each query at p sees A(p + 1) over the history including the chunk's own
@@ -137,7 +159,7 @@ def prefill_chunk(q: np.ndarray, n: int, hist: History, P: int, W: int, n_kv_hea
     rows = range(C) if rows is None else rows
     outs, lses = [], []
     for c in rows:
-        o, s = decode_query(q[c], n + c, hist, P, W, n_kv_heads, base, scale)
+        o, s = decode_query(q[c], n + c, hist, P, W, n_kv_heads, base, scale, pe)
         outs.append(o)
         lses.append(s)
     return np.stack(outs), np.stack(lses)

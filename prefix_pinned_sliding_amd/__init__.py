@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libpsa.so")
 
 PSA_OK, PSA_ERR_ARG, PSA_ERR_STATE, PSA_ERR_OVERFLOW, PSA_ERR_HIP = 0, 1, 2, 3, 4
 PSA_BF16, PSA_F32 = 0, 1
+PSA_PE_CONTINUE, PSA_PE_RESET = 0, 1
+_PE = {"continue": PSA_PE_CONTINUE, "reset": PSA_PE_RESET}
 K_APPEND, K_DECODE, K_MERGE, K_PREFILL_STAGE, K_PREFILL = 0, 1, 2, 3, 4
 KERNEL_NAMES = {K_APPEND: "append", K_DECODE: "decode_partial", K_MERGE: "merge",
                 K_PREFILL_STAGE: "prefill_stage", K_PREFILL: "prefill"}
@@ -40,6 +42,7 @@ class Desc(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("n_shared_prefixes", ctypes.c_int32),
         ("shared_prefix_max", ctypes.c_int32),
+        ("pe_mode", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -115,11 +118,14 @@ def _ptr(t: Optional[torch.Tensor]):
 def make_desc(max_batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, prefix_max: int,
               window: int, dtype: torch.dtype = torch.bfloat16, rope_base: float = 10000.0,
               scale: float = 0.0, max_chunk: int = 0, n_shared_prefixes: int = 0,
-              shared_prefix_max: int = 0) -> Desc:
+              shared_prefix_max: int = 0, pe: str = "continue") -> Desc:
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {dtype}")
+    if pe not in _PE:
+        raise ValueError(f"pe must be one of {list(_PE)}")
     return Desc(max_batch, n_q_heads, n_kv_heads, head_dim, prefix_max, window, _DTYPES[dtype],
-                max_chunk, float(rope_base), float(scale), n_shared_prefixes, shared_prefix_max, 0)
+                max_chunk, float(rope_base), float(scale), n_shared_prefixes, shared_prefix_max,
+                _PE[pe], 0)
 
 
 def cache_bytes(desc: Desc) -> int:
@@ -147,10 +153,12 @@ class Cache:
     def __init__(self, max_batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  prefix_max: int, window: int, dtype: torch.dtype = torch.bfloat16,
                  rope_base: float = 10000.0, scale: float = 0.0, max_chunk: int = 0,
-                 device=None, stream=None, n_shared_prefixes: int = 0, shared_prefix_max: int = 0):
+                 device=None, stream=None, n_shared_prefixes: int = 0, shared_prefix_max: int = 0,
+                 pe: str = "continue"):
         self.desc = make_desc(max_batch, n_q_heads, n_kv_heads, head_dim, prefix_max, window,
                               dtype, rope_base, scale, max_chunk, n_shared_prefixes,
-                              shared_prefix_max)
+                              shared_prefix_max, pe)
+        self.pe = pe
         self.n_shared, self.shared_max = n_shared_prefixes, shared_prefix_max
         self.dtype = dtype
         self.B, self.Hq, self.Hkv, self.D = max_batch, n_q_heads, n_kv_heads, head_dim

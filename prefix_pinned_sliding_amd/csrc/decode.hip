@@ -148,10 +148,26 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     const int n_pre = min(n, P);
     const int n_win = min(c.W, max(0, n - P));
     const int Tb = n_pre + n_win;
-    const int ns = (Tb + split_tokens - 1) / split_tokens;
+    const int ns = split_count(n_pre, n_win, split_tokens, c.pe_mode);
     if (split >= ns) return;
-    const int i0 = split * split_tokens;
-    const int i1 = min(Tb, i0 + split_tokens);
+    int i0, i1;
+    int qpos = n - 1;                 // position the query is rotated at
+    if (c.pe_mode == PSA_PE_RESET) {
+        // prefix splits first, then window splits; prefix keys see the query at its
+        // renumbered position P + n_win - 1 (the newest window entry's)
+        const int ns_pre = (n_pre + split_tokens - 1) / split_tokens;
+        if (split < ns_pre) {
+            i0 = split * split_tokens;
+            i1 = min(n_pre, i0 + split_tokens);
+            if (n_win > 0) qpos = P + n_win - 1;
+        } else {
+            i0 = n_pre + (split - ns_pre) * split_tokens;
+            i1 = min(Tb, i0 + split_tokens);
+        }
+    } else {
+        i0 = split * split_tokens;
+        i1 = min(Tb, i0 + split_tokens);
+    }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane % LPK, grp = lane / LPK;
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     if (base_i < i1) load(nxt, base_i);
 
     {
-        const int p = n - 1;
+        const int p = qpos;
         const float sc = c.scale * kLog2e;
         for (int idx = tid; idx < G * (D / 2); idx += kBlock) {
             const int g = idx / (D / 2), i = idx % (D / 2);
@@ -336,8 +352,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DevCache c, typename Elem<DT>:
     const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int n = len_cur[b];
     const int P = c.pre[b];
-    const int Tb = min(n, P) + min(c.W, max(0, n - P));
-    const int ns = (Tb + split_tokens - 1) / split_tokens;
+    const int ns = split_count(min(n, P), min(c.W, max(0, n - P)), split_tokens, c.pe_mode);
     const size_t base = ((size_t)b * c.Hq + hq) * c.max_splits;
     const float* ml = c.part_ml + base * 2;
     float M = -INFINITY;

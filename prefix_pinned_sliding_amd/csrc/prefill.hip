@@ -77,6 +77,14 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
     const int p = len_cur[b] + j;
     double sn, cs;
     angle_sincos(p, c.inv_freq[i], &sn, &cs);
+    // RESET: for prefix keys the query sits at its renumbered position min(p, P + W - 1)
+    const bool reset = c.pe_mode == PSA_PE_RESET;
+    double snp = sn, csp = cs;
+    if (reset) {
+        const int P = c.pre[b];
+        const int pp = p < P ? p : P + min(c.W, p + 1 - P) - 1;
+        if (pp != p) angle_sincos(pp, c.inv_freq[i], &snp, &csp);
+    }
     const size_t tok = (size_t)b * chunk + j;
     const double sc = (double)c.scale * (double)kLog2e;
     const int h_end = min(heads, (grp + 1) * kStageHeads);
@@ -95,6 +103,14 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
             uint16_t* qo = (uint16_t*)c.stage_q;
             qo[off + i] = q_to_bf16(xr * sc);
             qo[off + i + H] = q_to_bf16(yr * sc);
+            if (reset) {
+                double xp, yp;
+                rotate_with(bf16_bits_to_f64(src[off + i]), bf16_bits_to_f64(src[off + i + H]),
+                            snp, csp, &xp, &yp);
+                uint16_t* qp = (uint16_t*)c.stage_qp;
+                qp[off + i] = q_to_bf16(xp * sc);
+                qp[off + i + H] = q_to_bf16(yp * sc);
+            }
         }
     }
 }
@@ -115,22 +131,28 @@ __device__ __forceinline__ float row_sum4(float x) {
     return x;
 }
 
-// The three key ranges of a workgroup and the first row's window start; `next` steps
-// (seg, t0) to the next tile that some row of the workgroup sees.
+// The key ranges of a workgroup, in walk order: 0 = prefix in the cache, 1 = prefix
+// tokens inside the chunk (n < P), 2 = still-visible ring (n > P), 3 = window tokens of
+// the chunk. Prefix keys (ranges 0, 1) all come before window keys (2, 3). `win_lo` is
+// the first row's window start; walk_next steps (seg, t0) to the next tile some row sees.
 struct Walk {
-    int hi0, lo1, hi1, lo2, hi2, P, win_lo;
-    __device__ int lo(int seg) const { return seg == 1 ? lo1 : (seg == 2 ? lo2 : 0); }
-    __device__ int hi(int seg) const { return seg == 0 ? hi0 : (seg == 1 ? hi1 : hi2); }
+    int hi0, lo1, hi1, lo2, hi2, lo3, hi3, P, win_lo;
+    __device__ int lo(int seg) const {
+        return seg == 1 ? lo1 : (seg == 2 ? lo2 : (seg == 3 ? lo3 : 0));
+    }
+    __device__ int hi(int seg) const {
+        return seg == 0 ? hi0 : (seg == 1 ? hi1 : (seg == 2 ? hi2 : hi3));
+    }
 };
 
 template <int BN>
 __device__ __forceinline__ bool walk_next(const Walk& w, int& seg, int& t0) {
     t0 += BN;
-    while (seg < 3) {
+    while (seg < 4) {
         const int hi = w.hi(seg);
         if (t0 >= hi) {
             ++seg;
-            if (seg < 3) t0 = w.lo(seg);
+            if (seg < 4) t0 = w.lo(seg);
             continue;
         }
         const int t1 = min(t0 + BN, hi);
@@ -166,12 +188,12 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
     const uint16_t* kb;
     const uint16_t* vb;
     int stride, ring0 = 0;
-    if (seg == 2) {
+    if (seg == 1 || seg == 3) {
         const size_t o = ((s.chunk_row0 + (size_t)(t0 - s.n)) * s.Hkv + s.h) * D;
         kb = s.k_chunk + o;
         vb = s.v_chunk + o;
         stride = s.Hkv * D;
-    } else if (seg == 1) {
+    } else if (seg == 2) {
         kb = s.k_cache + (size_t)s.Pmax * D;
         vb = s.v_cache + (size_t)s.Pmax * D;
         stride = D;
@@ -182,7 +204,7 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
         stride = D;
     }
     auto row = [&](int off) -> int {   // row index relative to the tile's base pointer
-        if (seg != 1) return off;
+        if (seg != 2) return off;
         const int r = ring0 + off;
         return s.W >= BN ? (r >= s.W ? r - s.W : r) : r % s.W;
     };
@@ -286,18 +308,22 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 
     // rows of this lane: r = 32 * wave + 16 * rb + l16, position p = n + c0 + r / G
     int row_pos[2];
+    size_t q_off[2];
     bf16x8 qop[2][KS];
-    const uint16_t* stage_q = (const uint16_t*)c.stage_q;
+    // RESET: prefix tiles come first and use the queries rotated at their renumbered
+    // positions; the operands are swapped once the walk leaves the prefix.
+    bool q_prefix = c.pe_mode == PSA_PE_RESET;
+    const uint16_t* stage_q = (const uint16_t*)(q_prefix ? c.stage_qp : c.stage_q);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int r = 32 * wave + 16 * rb + l16;
         const int cl = min(c0 + r / G, chunk - 1);
         const int g = r % G;
         row_pos[rb] = n + c0 + r / G;
-        const uint16_t* qrow = stage_q + (((size_t)b * chunk + cl) * c.Hq + h * G + g) * D;
+        q_off[rb] = (((size_t)b * chunk + cl) * c.Hq + h * G + g) * D + 8 * lg;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32 + 8 * lg));
+            qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage_q + q_off[rb] + ks * 32));
     }
 
     f32x4 o[2][DB];
@@ -312,12 +338,12 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 
     const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
 
-    // Key ranges in position space: 0 = prefix (cache), 1 = still-visible ring (cache),
-    // 2 = the chunk (staged keys, input values).
+    // Key ranges in position space (see Walk).
     const int nA = min(n, P);
-    const int lo1 = n > P ? max(P, p_lo - W + 1) : n;
-    const int lo2 = n, hi2 = p_hi + 1;
-    const Walk wk{nA, lo1, n, lo2, hi2, P, p_lo - W + 1};
+    const int hi1 = min(P, p_hi + 1);                  // chunk prefix: [n, hi1) when n < P
+    const int lo2 = n > P ? max(P, p_lo - W + 1) : n;  // ring: [lo2, n) when n > P
+    const int lo3 = max(n, P);                         // chunk window: [lo3, p_hi]
+    const Walk wk{nA, n, hi1, lo2, n, lo3, p_hi + 1, P, p_lo - W + 1};
     const int pid = c.pid[b];
     const size_t pre_off = pid >= 0 ? ((size_t)pid * c.Hkv + h) * (size_t)c.shared_max * D : head_off;
     const TileSrc src{(const uint16_t*)c.k + head_off, (const uint16_t*)c.v + head_off,
@@ -334,6 +360,15 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 #pragma unroll 1
     while (have) {
         const int cseg = seg, ct0 = t0;
+        if (q_prefix && cseg >= 2) {
+            const uint16_t* sq = (const uint16_t*)c.stage_q;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(sq + q_off[rb] + ks * 32));
+            q_prefix = false;
+        }
         const int t1 = min(ct0 + kBN, wk.hi(cseg));
         const bool full = (ct0 + kBN == t1) && (t1 - 1 <= p_lo) &&
                           (t1 - 1 < P || ct0 >= p_hi - W + 1);

@@ -76,13 +76,16 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     if (d.n_shared_prefixes > 0 && d.shared_prefix_max < 1)
         return bad("shared_prefix_max must be >= 1 when the pool has entries");
     if ((int64_t)d.shared_prefix_max + d.window > (1 << 30)) return bad("shared_prefix_max too large");
+    if (d.pe_mode != PSA_PE_CONTINUE && d.pe_mode != PSA_PE_RESET)
+        return bad("pe_mode must be PSA_PE_CONTINUE or PSA_PE_RESET");
     if (d.reserved != 0) return bad("reserved must be 0");
     const int64_t S = (int64_t)d.prefix_max + d.window;
     if (S > (1 << 30)) return bad("prefix_max + window too large");
     const size_t elem = d.dtype == PSA_BF16 ? 2 : 4;
     const size_t B = (size_t)d.max_batch, Hq = (size_t)d.n_q_heads, Hkv = (size_t)d.n_kv_heads;
     const size_t D = (size_t)d.head_dim;
-    const int64_t max_splits = (S + kSplitGranule - 1) / kSplitGranule;
+    // RESET splits the prefix and the window separately: one more split at most.
+    const int64_t max_splits = (S + kSplitGranule - 1) / kSplitGranule + 1;
     const size_t A = 256;
     size_t off = 0;
     L->k = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
@@ -97,6 +100,8 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
     L->stage_k = off;  off = align_up(off + B * (size_t)d.max_chunk * Hkv * D * elem, A);
     L->stage_q = off;  off = align_up(off + B * (size_t)d.max_chunk * Hq * D * 2, A);
+    L->stage_qp = off;
+    off = align_up(off + (d.pe_mode == PSA_PE_RESET ? B * (size_t)d.max_chunk * Hq * D * 2 : 0), A);
     L->total = off;
     L->S = (int32_t)S;
     L->elem = (int32_t)elem;
@@ -248,6 +253,7 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.part_ml = (float*)(base + L.part_ml);
     d.stage_k = base + L.stage_k;
     d.stage_q = base + L.stage_q;
+    d.stage_qp = base + L.stage_qp;
     d.B = desc->max_batch;
     d.Hq = desc->n_q_heads;
     d.Hkv = desc->n_kv_heads;
@@ -260,6 +266,7 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.max_splits = L.max_splits;
     d.n_shared = desc->n_shared_prefixes;
     d.shared_max = desc->shared_prefix_max;
+    d.pe_mode = desc->pe_mode;
     d.scale = desc->scale > 0.f ? desc->scale : (float)(1.0 / sqrt((double)desc->head_dim));
 
     // theta_i = base^(-2i/D) in float64 on the host.
@@ -389,7 +396,9 @@ PSA_API int psa_decode_attn(psa_cache* c, const void* q, void* out, float* lse, 
     const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
     int64_t max_ns = 1;
     for (int b = 0; b < B; ++b) {
-        const int64_t ns = (visible_count(c, b) + L - 1) / L;
+        const int64_t n_pre = c->len[b] < c->pre[b] ? c->len[b] : c->pre[b];
+        const int64_t ns =
+            psa::split_count((int)n_pre, (int)(visible_count(c, b) - n_pre), L, c->desc.pe_mode);
         if (ns > max_ns) max_ns = ns;
     }
     hipStream_t s = (hipStream_t)stream;

@@ -28,12 +28,14 @@ struct DevCache {
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
     void* stage_k;       // [B][max_chunk][Hkv][D] rotated prefill-chunk keys (stored bytes)
     void* stage_q;       // [B][max_chunk][Hq][D] rotated, scaled prefill-chunk queries (bf16)
-    int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits, n_shared, shared_max;
+    void* stage_qp;      // same, rotated at the renumbered position for prefix keys (RESET)
+    int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits, n_shared, shared_max, pe_mode;
     float scale;
 };
 
 struct Layout {
-    size_t k, v, pool_k, pool_v, tags, state, inv_freq, part_o, part_ml, stage_k, stage_q, total;
+    size_t k, v, pool_k, pool_v, tags, state, inv_freq, part_o, part_ml, stage_k, stage_q, stage_qp,
+        total;
     int32_t S, elem, max_splits;
 };
 
@@ -53,6 +55,14 @@ hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_
                          int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s);
 hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
                                  int grid_splits, int cur, hipStream_t s);
+// Decode splits of a sequence with n_pre prefix and n_win window entries. CONTINUE cuts the
+// concatenated list; RESET cuts the prefix and the window separately, so a split never
+// mixes keys that need differently rotated queries.
+__host__ __device__ inline int split_count(int n_pre, int n_win, int L, int pe_mode) {
+    if (pe_mode == PSA_PE_RESET) return (n_pre + L - 1) / L + (n_win + L - 1) / L;
+    return (n_pre + n_win + L - 1) / L;
+}
+
 // Workgroups of the decode kernel (for this cache's shape) that fit on the device at once.
 int decode_resident_wgs(const DevCache& c);
 hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,
