@@ -132,6 +132,32 @@ def decode_query_from_cache(q: np.ndarray, p: int, hist: History, P: int, W: int
     return out, lse
 
 
+def attend_list(q: np.ndarray, p: int, hist: History, positions, n_kv_heads: int, base: float,
+                scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of the query at position p over an explicit list of cached positions.
+
+    For caches whose content is not a closed-form set (a window whose length changed, or
+    promoted tokens), the list comes from the list model (spec.WindowModel); the logits
+    of every position not in the list are -inf ([KV-Lean] 2.1: masked positions get zero
+    weight), so only the listed ones are fetched.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Hq, D = q.shape
+    G = Hq // n_kv_heads
+    pos = np.asarray(sorted(positions), dtype=np.int64)
+    k, v = hist(pos)
+    qr = rope.rotate(q, np.full(Hq, p), base)
+    kr = rope.rotate(k, np.broadcast_to(pos[:, None], k.shape[:2]), base)
+    out = np.empty((Hq, D))
+    lse = np.empty(Hq)
+    for hq in range(Hq):
+        hk = hq // G
+        logits = np.full(p + 1, -np.inf)
+        logits[pos] = (kr[:, hk, :] @ qr[hq]) * scale
+        out[hq], lse[hq] = _softmax_attend(logits, v[:, hk, :], rows=pos)
+    return out, lse
+
+
 def decode_batch(q: np.ndarray, positions, hists, prefixes, W: int, n_kv_heads: int,
                  base: float, scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """decode_query for every sequence: q[B, H_q, D], positions[B], hists[B], prefixes[B]."""

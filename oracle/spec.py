@@ -152,3 +152,51 @@ class RingCache:
         nw = self.count_window()
         head = (window_base(self.P, self.W, self.n) - self.P) % self.W
         return list(self.prefix) + ring_to_list(self.ring, head, nw)
+
+
+class WindowModel:
+    """List model with a per-step window length and promotion into the pinned list.
+
+    [PS] 14 asks whether the window length could change during generation and whether
+    tokens could be promoted into the pinned prefix. The reading taken here generalises
+    the list model of [KV-Lean] 2.2 and 3.3 with w as a per-step parameter:
+
+    * a token at position < P joins the pinned prefix; any other token is appended to the
+      window, which then drops its oldest entries while longer than the current w;
+    * set_window(w) makes w the length from now on and drops the oldest entries beyond it
+      at once (dropped tokens never come back, even if w later grows);
+    * promote(k) moves the k oldest window entries to the end of the pinned list, where
+      they stay for good; the window keeps the rest.
+
+    The query at the newest position attends to pinned + window.
+    """
+
+    def __init__(self, P: int, w: int):
+        if w < 1:
+            raise ValueError("window must be at least 1")
+        self.P, self.w = P, w
+        self.pinned: list = []
+        self.window: list = []
+        self.n = 0
+
+    def push(self, kv) -> None:
+        if self.n < self.P:
+            self.pinned.append(kv)
+        else:
+            self.window = step(self.w, self.window, kv)
+        self.n += 1
+
+    def set_window(self, w: int) -> None:
+        if w < 1:
+            raise ValueError("window must be at least 1")
+        self.w = w
+        self.window = last_window(w, self.window)
+
+    def promote(self, k: int) -> None:
+        if k < 0 or k > len(self.window):
+            raise ValueError("cannot promote more entries than the window holds")
+        self.pinned = self.pinned + self.window[:k]
+        self.window = self.window[k:]
+
+    def view(self) -> list:
+        return list(self.pinned) + list(self.window)
