@@ -132,22 +132,31 @@ def decode_query_from_cache(q: np.ndarray, p: int, hist: History, P: int, W: int
     return out, lse
 
 
-def attend_list(q: np.ndarray, p: int, hist: History, positions, n_kv_heads: int, base: float,
-                scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """Attention of the query at position p over an explicit list of cached positions.
+def attend_view(q: np.ndarray, p: int, hist: History, view, n_kv_heads: int, base: float,
+                scale: float, pe: str = "continue") -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of the query at position p over an explicit cache list.
 
-    For caches whose content is not a closed-form set (a window whose length changed, or
-    promoted tokens), the list comes from the list model (spec.WindowModel); the logits
-    of every position not in the list are -inf ([KV-Lean] 2.1: masked positions get zero
-    weight), so only the listed ones are fetched.
+    `view` is the list model's cache after token p, in list order (pinned entries, then
+    the window, oldest first), as absolute positions; spec.WindowModel gives it for
+    caches that are not a closed-form set (a window whose length changed, promoted
+    tokens). Every position not in the list has logit -inf ([KV-Lean] 2.1: masked
+    positions get zero weight), so only the listed ones are fetched.
+
+    "continue" rotates at absolute positions. "reset" ([PS] 05) renumbers the attended
+    list as one sequence: entry i of `view` gets position i and the query, the newest
+    entry, len(view) - 1; on the closed-form set this is `reset_positions`.
     """
     q = np.asarray(q, dtype=np.float64)
     Hq, D = q.shape
     G = Hq // n_kv_heads
-    pos = np.asarray(sorted(positions), dtype=np.int64)
+    pos = np.asarray(list(view), dtype=np.int64)
     k, v = hist(pos)
-    qr = rope.rotate(q, np.full(Hq, p), base)
-    kr = rope.rotate(k, np.broadcast_to(pos[:, None], k.shape[:2]), base)
+    if pe == "continue":
+        qpos, kpos = p, pos
+    else:
+        qpos, kpos = len(pos) - 1, np.arange(len(pos))
+    qr = rope.rotate(q, np.full(Hq, qpos), base)
+    kr = rope.rotate(k, np.broadcast_to(kpos[:, None], k.shape[:2]), base)
     out = np.empty((Hq, D))
     lse = np.empty(Hq)
     for hq in range(Hq):

@@ -1,7 +1,7 @@
 """Pins of spec.WindowModel (per-step window length, promotion) and attn.attend_list."""
 import numpy as np
 
-from oracle import attn, spec
+from oracle import attn, rope, spec
 from oracle.spec import Cell
 
 
@@ -53,15 +53,62 @@ def test_promotion_moves_oldest_window_entries():
     assert [c.pos for c in m.view()] == [0, 1, 6, 7, 12, 13, 14, 15]
 
 
-def test_attend_list_equals_mask_form_for_the_closed_form_set():
+def test_attend_view_equals_mask_form_for_the_closed_form_set():
+    # Both PE modes: on the closed-form set the list form must match the mask form
+    # (continue) and reset_positions (reset), including queries inside the prefix.
     rng = np.random.default_rng(1)
     k = rng.standard_normal((80, 2, 16))
     v = rng.standard_normal((80, 2, 16))
     h = attn.array_history(k, v)
-    for p in (5, 30, 79):
-        q = rng.standard_normal((4, 16))
-        pos = spec.pinned_view(3, 20, range(p + 1))
-        a = attn.attend_list(q, p, h, pos, 2, 10000.0, 0.25)
-        b = attn.decode_query(q, p, h, 3, 20, 2, 10000.0, 0.25)
-        np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-12)
-        np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-12)
+    for pe in ("continue", "reset"):
+        for p in (1, 5, 30, 79):
+            q = rng.standard_normal((4, 16))
+            pos = spec.pinned_view(3, 20, range(p + 1))
+            a = attn.attend_view(q, p, h, pos, 2, 10000.0, 0.25, pe)
+            b = attn.decode_query(q, p, h, 3, 20, 2, 10000.0, 0.25, pe)
+            np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-12)
+
+
+def test_attend_view_shrunk_window_is_a_smaller_window():
+    # A window shrunk to w at once and then filled again equals the constant window w
+    # once w new tokens have arrived (every older entry has left either way).
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((120, 2, 16))
+    v = rng.standard_normal((120, 2, 16))
+    h = attn.array_history(k, v)
+    m = spec.WindowModel(4, 40)
+    for p in range(60):
+        m.push(p)
+    m.set_window(9)
+    for p in range(60, 100):
+        m.push(p)
+        if p >= 69:
+            q = rng.standard_normal((4, 16))
+            a = attn.attend_view(q, p, h, m.view(), 2, 10000.0, 0.25)
+            b = attn.decode_query(q, p, h, 4, 9, 2, 10000.0, 0.25)
+            np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-12)
+
+
+def test_promoted_tokens_stay_visible():
+    # After promotion the promoted positions are attended forever: the output equals the
+    # mask form with those positions forced visible (a hand-built logit mask).
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((90, 1, 8))
+    v = rng.standard_normal((90, 1, 8))
+    h = attn.array_history(k, v)
+    m = spec.WindowModel(2, 6)
+    for p in range(20):
+        m.push(p)
+    m.promote(3)                      # positions 14, 15, 16
+    for p in range(20, 90):
+        m.push(p)
+    q = rng.standard_normal((1, 8))
+    out, lse = attn.attend_view(q, 89, h, m.view(), 1, 10000.0, 1.0)
+    keep = [0, 1, 14, 15, 16] + list(range(84, 90))
+    qr = rope.rotate(q, np.full(1, 89), 10000.0)[0]
+    kr = rope.rotate(k[keep], np.asarray(keep)[:, None], 10000.0)[:, 0]
+    s = kr @ qr
+    w = np.exp(s - s.max())
+    np.testing.assert_allclose(out[0], (w / w.sum()) @ v[keep, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], s.max() + np.log(w.sum()), rtol=0, atol=1e-12)
