@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p100_w4096",
                     choices=["decode_p100_w4096", "decode_p512_w16384", "ragged_decode",
-                             "decode_shared_p2000", "decode_private_p2000"])
+                             "decode_shared_p2000", "decode_private_p2000",
+                             "decode_ragged_window"])
     ap.add_argument("--t", type=int, default=0, help="override the start position t (flat-in-t sweeps)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--pe", default="continue", choices=["continue", "reset"],
@@ -82,7 +83,7 @@ def cpu_baseline(wl, n_now, q_rows, budget_s: float):
     def prepared(b):
         full = drive.hist_provider(wl, b)
         p = n_now[b] - 1
-        pos = np.nonzero(attn.visible_mask(wl.prefix[b], wl.window, p))[0]
+        pos = np.nonzero(attn.visible_mask(wl.prefix[b], wl.window_of(b), p))[0]
         k, v = full(pos)
         key = pos.tobytes()
 
@@ -98,7 +99,7 @@ def cpu_baseline(wl, n_now, q_rows, budget_s: float):
             b = done
             h = prepared(b)
             t0 = time.perf_counter()
-            attn.decode_query(q_rows[b], n_now[b] - 1, h, wl.prefix[b], wl.window,
+            attn.decode_query(q_rows[b], n_now[b] - 1, h, wl.prefix[b], wl.window_of(b),
                               wl.n_kv_heads, wl.rope_base, wl.scale)
             elapsed += time.perf_counter() - t0
             done += 1
@@ -196,6 +197,8 @@ def main():
         wl = configs.decode_shared_p2000(t=args.t) if args.t else configs.decode_shared_p2000()
         if args.workload == "decode_private_p2000":
             wl.name = wl.name.replace("shared", "private")
+    elif args.workload == "decode_ragged_window":
+        wl = configs.decode_ragged_window(t=args.t) if args.t else configs.decode_ragged_window()
     else:
         wl = configs.ragged_decode()
     B = wl.batch
@@ -278,7 +281,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
                    "prefix": wl.prefix[0] if len(set(wl.prefix)) == 1 else "ragged",
-                   "window": wl.window, "t": wl.start[0] if len(set(wl.start)) == 1 else "ragged",
+                   "window": wl.window if wl.windows is None else "ragged",
+                   "t": wl.start[0] if len(set(wl.start)) == 1 else "ragged",
                    "visible_tokens_per_step": vis, "parallelism": "single GPU",
                    "position_encoding": args.pe},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -13,6 +13,9 @@
  *             cache: 2.2-2.4 window list model and slot positions, 3.2 cells with
  *             positions, 3.3 step, 3.4 ring buffer read as a list, 5.1 not-full
  *             pitfalls, 6.3 export-and-compare checks.
+ *   [PS] 14 (open questions: how coarse the pinned prefix should be, whether the window
+ *             could change while generating) motivates psa_seq_set_window and
+ *             psa_seq_promote.
  *
  * Conventions used by every call:
  *   - Positions are 0-based absolute token positions p (p = t - 1 for the pages'
@@ -20,7 +23,9 @@
  *   - The query at position p attends to key j iff j <= p and (j < P_b or
  *     j >= p - W + 1): the pinned prefix [1, P] and the window
  *     [max(P + 1, t - W + 1), t] of [PS] 03. A query inside the prefix (p < P_b)
- *     attends causally to [0, p].
+ *     attends causally to [0, p]. W is the sequence's window length w_b (desc.window
+ *     unless psa_seq_set_window changed it); after a window change or a promotion the
+ *     attended set is the list model's cache (see those calls).
  *   - Keys are rotated (rotary position encoding, rotate-half pairing (i, i + D/2),
  *     theta_i = rope_base^(-2i/D)) at their absolute position once, when appended,
  *     and reused as stored ([PS] 05, "Continue PE"). The rotation is computed in
@@ -73,7 +78,7 @@ typedef struct {
     int32_t n_kv_heads;  /* H_kv >= 1 */
     int32_t head_dim;    /* D: 64 or 128 */
     int32_t prefix_max;  /* P_max >= 0: largest pinned-prefix length any sequence may use */
-    int32_t window;      /* W >= 1: window length */
+    int32_t window;      /* W >= 1: window length (the largest psa_seq_set_window accepts) */
     int32_t dtype;       /* PSA_BF16 or PSA_F32 (storage, inputs and outputs) */
     int32_t max_chunk;   /* largest prefill chunk C (0: psa_prefill_attn unavailable) */
     double rope_base;    /* > 0, e.g. 10000 */
@@ -97,9 +102,11 @@ enum { PSA_PE_CONTINUE = 0, PSA_PE_RESET = 1 };
 
 /* Byte offsets of the regions the library carves out of the caller's device buffer.
  * K and V: [B][H_kv][S][D] with S = prefix_max + window slots per (sequence, head):
- * slots [0, P_max) hold prefix positions p < P_b at slot p; slots [P_max, S) are the
- * ring, position p >= P_b at slot P_max + (p - P_b) mod W.
- * tags: [B][S] int32, the absolute position held by each slot, -1 if never written.
+ * slots [0, P_max) hold prefix positions p < P_b at slot p (promoted entries follow at
+ * slots P_b, P_b + 1, ...); slots [P_max, S) are the ring, position p >= P_b at slot
+ * P_max + (p - P_b) mod W.
+ * tags: [B][S] int32, the absolute position held by each slot, -1 if it holds no cached
+ * entry (never written, or its entry left the cache without being overwritten).
  * pool K and V: [n_shared_prefixes][H_kv][shared_prefix_max][D], position p of entry e
  * at row p (absent when n_shared_prefixes is 0). */
 typedef struct {
@@ -160,14 +167,41 @@ int psa_prefix_load(psa_cache *cache, int32_t prefix_id, int32_t len, const void
  * loaded; PSA_ERR_ARG for an out-of-range id. */
 int psa_seq_attach(psa_cache *cache, int32_t seq, int32_t prefix_id, psa_stream stream);
 
+/* Window length and promotion of one sequence (host checks, then a small kernel on
+ * `stream`). The sequence's cache follows a list model: a pinned list and a window list
+ * (oldest first). An append puts the token into the pinned list while p < P_b, else at
+ * the window's tail, dropping the window's oldest entries while it holds more than w_b.
+ *
+ * psa_seq_set_window: w_b = window (1 <= window <= desc.window) from now on; a window
+ * holding more entries drops its oldest ones at once. Dropped entries never come back,
+ * so after a growth the window refills with new tokens only. No K/V bytes move.
+ * Errors: PSA_ERR_ARG for a window out of range; PSA_ERR_STATE if `seq` was never reset
+ * (psa_seq_reset and psa_seq_attach restore w_b = desc.window). */
+int psa_seq_set_window(psa_cache *cache, int32_t seq, int32_t window, psa_stream stream);
+
+/* psa_seq_promote: move the `count` oldest window entries to the end of the pinned list,
+ * where they stay for good (their keys keep the rotation of their absolute positions;
+ * they are copied to the next free prefix slots). Errors: PSA_ERR_ARG if count is
+ * negative, exceeds the window's entries, or the pinned list would exceed prefix_max;
+ * PSA_ERR_STATE if `seq` was never reset, reads a shared prefix (psa_seq_attach), or the
+ * cache uses PSA_PE_RESET (renumbered positions are defined for [prefix, window] only). */
+int psa_seq_promote(psa_cache *cache, int32_t seq, int32_t count, psa_stream stream);
+
+/* From the host mirror: the sequence's window length, its pinned entries (min(n, P_b)
+ * plus promoted ones) and its window entries; any output may be NULL. Host only.
+ * Errors: PSA_ERR_STATE if `seq` is out of range or was never reset. */
+int psa_seq_window(const psa_cache *cache, int32_t seq, int32_t *window, int32_t *pinned,
+                   int32_t *window_entries);
+
 /* Append new tokens to every sequence ([PS] 03 generation loop; [KV-Lean] 2.2, 3.3:
  * append at the tail, evict the oldest once the window holds more than W).
  * k, v: [B][n_stride][H_kv][D]. Sequence b appends n_b tokens, rows 0 .. n_b - 1 of
  * its block, at positions len_b, len_b + 1, ...: n_b = n_new_host[b] if n_new_host is
  * not NULL (a host array of B entries), else n_uniform. 0 <= n_b <= n_stride.
  * A token at p < P_b goes to prefix slot p; otherwise to ring slot (p - P_b) mod W,
- * overwriting (evicting) position p - W. The key is stored rotated at p. A token that
- * a later token of the same call evicts is not written.
+ * overwriting (evicting) position p - W; with w_b < W the window's oldest entries leave
+ * by the length rule and their slots get tag -1. The key is stored rotated at p. A token
+ * that a later token of the same call evicts is not written.
  * Errors: PSA_ERR_STATE if a sequence with n_b > 0 was never reset;
  * PSA_ERR_OVERFLOW if len_b + n_b > INT32_MAX. */
 int psa_append(psa_cache *cache, const int32_t *n_new_host, int32_t n_uniform, const void *k,
@@ -191,12 +225,12 @@ int psa_prefill_attn(psa_cache *cache, int32_t chunk, const void *q, const void 
                      const void *v, void *out, float *lse, psa_stream stream);
 
 /* Copy sequence `seq`'s logical cache to host memory ([KV-Lean] 3.4 ring read back
- * as a list; 6.3 export and compare against the list model): the prefix entries (from
- * the pool for an attached sequence), then the window oldest first,
- * count = min(len, P_b + W) entries. k_host, v_host:
- * [S][H_kv][D] (capacity S = max(prefix_max, shared_prefix_max) + window entries),
- * pos_host: [S] int32
- * absolute positions; any of the three may be NULL. Waits for `stream`. */
+ * as a list; 6.3 export and compare against the list model): the pinned entries (from
+ * the pool for an attached sequence), then the window oldest first; count = pinned +
+ * window entries (min(len, P_b + W) unless the window length changed or entries were
+ * promoted). k_host, v_host: [S][H_kv][D] (capacity S = max(prefix_max,
+ * shared_prefix_max) + window entries), pos_host: [S] int32 absolute positions; any of
+ * the three may be NULL. Waits for `stream`. */
 int psa_export(psa_cache *cache, int32_t seq, void *k_host, void *v_host, int32_t *pos_host,
                int32_t *count, psa_stream stream);
 

@@ -77,6 +77,10 @@ def _load() -> ctypes.CDLL:
         "psa_seq_reset": (ctypes.c_int, [P, I32, I32, P]),
         "psa_prefix_load": (ctypes.c_int, [P, I32, I32, P, P, P]),
         "psa_seq_attach": (ctypes.c_int, [P, I32, I32, P]),
+        "psa_seq_set_window": (ctypes.c_int, [P, I32, I32, P]),
+        "psa_seq_promote": (ctypes.c_int, [P, I32, I32, P]),
+        "psa_seq_window": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                          ctypes.POINTER(I32)]),
         "psa_append": (ctypes.c_int, [P, P, I32, P, P, I32, P]),
         "psa_decode_attn": (ctypes.c_int, [P, P, P, P, P]),
         "psa_prefill_attn": (ctypes.c_int, [P, I32, P, P, P, P, P, P]),
@@ -214,6 +218,22 @@ class Cache:
     def attach(self, seq: int, prefix_id: int, stream=None) -> None:
         """Start sequence `seq` on shared-prefix entry `prefix_id`."""
         _check(lib.psa_seq_attach(self._h, seq, prefix_id, _stream(stream)), "psa_seq_attach")
+
+    def set_window(self, seq: int, window: int, stream=None) -> None:
+        """Window length of sequence `seq` from now on (1 .. W); a longer window drops its
+        oldest entries at once."""
+        _check(lib.psa_seq_set_window(self._h, seq, window, _stream(stream)), "psa_seq_set_window")
+
+    def promote(self, seq: int, count: int, stream=None) -> None:
+        """Move the `count` oldest window entries of `seq` into its pinned prefix."""
+        _check(lib.psa_seq_promote(self._h, seq, count, _stream(stream)), "psa_seq_promote")
+
+    def window_info(self, seq: int) -> Tuple[int, int, int]:
+        """(window length, pinned entries, window entries) of `seq` from the host mirror."""
+        w, pin, ent = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.psa_seq_window(self._h, seq, ctypes.byref(w), ctypes.byref(pin),
+                                  ctypes.byref(ent)), "psa_seq_window")
+        return w.value, pin.value, ent.value
 
     def _kv_check(self, t: torch.Tensor, name: str, heads: int) -> int:
         if t.dtype != self.dtype or not t.is_contiguous() or t.device.type != "cuda":

@@ -34,14 +34,60 @@ __global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_
     if (i < (size_t)B) pid[i] = -1;
 }
 
-__global__ void seq_reset_kernel(int32_t* tags, int S, int32_t* len_cur, int32_t* pre,
-                                 int32_t* pid, int seq, int prefix_len, int len0, int prefix_id) {
+// A new sequence pins its first prefix_len tokens and uses the full window length W.
+__global__ void seq_reset_kernel(DevCache c, int32_t* len_cur, int seq, int prefix_len, int len0,
+                                 int prefix_id) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < S) tags[(size_t)seq * S + i] = -1;
+    if (i < c.S) c.tags[(size_t)seq * c.S + i] = -1;
     if (i == 0) {
         len_cur[seq] = len0;
-        pre[seq] = prefix_len;
-        pid[seq] = prefix_id;
+        c.pre[seq] = prefix_len;
+        c.pid[seq] = prefix_id;
+        c.npin[seq] = prefix_len;
+        c.wfloor[seq] = prefix_len;
+        c.wlen[seq] = c.W;
+    }
+}
+
+// New window length and floor; the ring positions [lo, hi) leave the window (their slots
+// are not reused by the new window, so their tags go back to -1).
+__global__ void seq_window_kernel(DevCache c, int seq, int wlen, int wfloor, int lo, int hi) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int p = lo + i;
+    if (p < hi) c.tags[(size_t)seq * c.S + c.Pmax + (p - c.pre[seq]) % c.W] = -1;
+    if (i == 0) {
+        c.wlen[seq] = wlen;
+        c.wfloor[seq] = wfloor;
+    }
+}
+
+// Promotion copies the stored bytes of window positions [wb, wb + count) from their ring
+// slots to prefix slots npin, npin + 1, ...: keys are stored rotated at their absolute
+// positions, which they keep. One thread per (token, KV head, 4-byte word of a row).
+__global__ __launch_bounds__(kBlock) void promote_kernel(DevCache c, int seq, int wb, int count,
+                                                         int npin, int row_words) {
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t total = (size_t)count * c.Hkv * row_words;
+    if (idx >= total) return;
+    const int w = (int)(idx % row_words);
+    const size_t r = idx / row_words;
+    const int h = (int)(r % c.Hkv);
+    const int j = (int)(r / c.Hkv);
+    const int p = wb + j;
+    const int from = c.Pmax + (p - c.pre[seq]) % c.W;
+    const int to = npin + j;
+    const size_t head = ((size_t)seq * c.Hkv + h) * c.S;
+    uint32_t* K = (uint32_t*)c.k;
+    uint32_t* V = (uint32_t*)c.v;
+    K[(head + to) * row_words + w] = K[(head + from) * row_words + w];
+    V[(head + to) * row_words + w] = V[(head + from) * row_words + w];
+    if (h == 0 && w == 0) {
+        c.tags[(size_t)seq * c.S + to] = p;
+        c.tags[(size_t)seq * c.S + from] = -1;
+    }
+    if (idx == 0) {
+        c.npin[seq] = npin + count;
+        c.wfloor[seq] = wb + count;
     }
 }
 
@@ -76,9 +122,11 @@ __global__ __launch_bounds__(kBlock) void pool_load_kernel(DevCache c, int id, i
 // One thread per (sequence b, token j, KV head h, rotation pair i): a one-token append is
 // latency-bound, so every pair gets its own thread (each computes its angle's sin/cos).
 // Token j of sequence b has position p = len[b] + j. Slot: p < P_b -> prefix slot p;
-// else ring slot P_max + (p - P_b) mod W. A ring token that a later token of the same call
-// overwrites (p < len[b] + n_b - W) is not written, so the surviving writer of each slot is
-// unique.
+// else ring slot P_max + (p - P_b) mod W. The window after the call is [wb', n') with
+// wb' = max(wfloor, n' - w_b); a token older than wb' (dropped again within the call) is
+// not written, so the writer of each slot is unique. Window entries that the call drops
+// and whose slots no new token takes (possible when w_b < W) get tag -1: token j's thread
+// clears the j-th of them (there are at most n_b).
 template <int DT, int D>
 __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typename Elem<DT>::T* k,
                                                         const typename Elem<DT>::T* v, int n_stride,
@@ -104,11 +152,22 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
 
     const int p = L0 + j;
     const int P = c.pre[b];
+    const int wf = c.wfloor[b], wl = c.wlen[b];
+    const int n1 = L0 + nb;
+    const int wb1 = max(wf, n1 - wl);                // window base after the call
+    if (h == 0 && i == 0 && wl < c.W) {
+        const int e = max(wf, L0 - wl) + j;          // j-th entry leaving the window
+        if (e < min(L0, wb1)) {
+            const int d = (wb1 - e) % c.W;           // e's slot relative to wb1's, mod W
+            const int rel = d == 0 ? 0 : c.W - d;
+            if (rel >= n1 - wb1) c.tags[(size_t)b * c.S + c.Pmax + (e - P) % c.W] = -1;
+        }
+    }
     int slot;
     if (p < P) {
         slot = p;
     } else {
-        if (p < L0 + nb - c.W) return;             // evicted by a later token of this call
+        if (p < wb1) return;                         // dropped within this call
         slot = c.Pmax + (p - P) % c.W;
     }
     const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * D;
@@ -136,7 +195,8 @@ inline unsigned blocks_for(size_t n) { return (unsigned)((n + kBlock - 1) / kBlo
 
 hipError_t launch_init(const DevCache& c, hipStream_t s) {
     const size_t n_tags = (size_t)c.B * c.S;
-    const int n_zero = 4 * c.B;   // len[0], len[1], pre, nnew are contiguous
+    const int n_zero = 4 * c.B;   // len[0], len[1], pre, nnew are contiguous; the rest is set
+                                  // by the reset of each sequence
     const size_t n = n_tags > (size_t)n_zero ? n_tags : (size_t)n_zero;
     hipLaunchKernelGGL(init_kernel, dim3(blocks_for(n)), dim3(kBlock), 0, s, c.tags, n_tags,
                        c.len[0], n_zero, c.pid, c.B);
@@ -145,8 +205,25 @@ hipError_t launch_init(const DevCache& c, hipStream_t s) {
 
 hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int len0, int pid, int cur,
                             hipStream_t s) {
-    hipLaunchKernelGGL(seq_reset_kernel, dim3(blocks_for((size_t)c.S)), dim3(kBlock), 0, s, c.tags,
-                       c.S, c.len[cur], c.pre, c.pid, seq, prefix_len, len0, pid);
+    hipLaunchKernelGGL(seq_reset_kernel, dim3(blocks_for((size_t)c.S)), dim3(kBlock), 0, s, c,
+                       c.len[cur], seq, prefix_len, len0, pid);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_window(const DevCache& c, int seq, int wlen, int wfloor, int clr_lo,
+                             int clr_hi, hipStream_t s) {
+    const int n = clr_hi > clr_lo ? clr_hi - clr_lo : 1;
+    hipLaunchKernelGGL(seq_window_kernel, dim3(blocks_for((size_t)n)), dim3(kBlock), 0, s, c, seq,
+                       wlen, wfloor, clr_lo, clr_hi);
+    return hipGetLastError();
+}
+
+hipError_t launch_promote(const DevCache& c, int seq, int wb, int count, int npin, hipStream_t s) {
+    const int row_words = c.D * (c.dtype == PSA_BF16 ? 2 : 4) / 4;
+    const size_t total = (size_t)count * c.Hkv * row_words;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(promote_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, c, seq, wb,
+                       count, npin, row_words);
     return hipGetLastError();
 }
 

@@ -144,9 +144,8 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int n = len_cur[b];
-    const int P = c.pre[b];
-    const int n_pre = min(n, P);
-    const int n_win = min(c.W, max(0, n - P));
+    const SeqView sv = seq_view(c, b, n);
+    const int n_pre = sv.n_pre, n_win = sv.n_win, ring_head = sv.head;
     const int Tb = n_pre + n_win;
     const int ns = split_count(n_pre, n_win, split_tokens, c.pe_mode);
     if (split >= ns) return;
@@ -154,12 +153,12 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     int qpos = n - 1;                 // position the query is rotated at
     if (c.pe_mode == PSA_PE_RESET) {
         // prefix splits first, then window splits; prefix keys see the query at its
-        // renumbered position P + n_win - 1 (the newest window entry's)
+        // renumbered position n_pre + n_win - 1 (the newest window entry's)
         const int ns_pre = (n_pre + split_tokens - 1) / split_tokens;
         if (split < ns_pre) {
             i0 = split * split_tokens;
             i1 = min(n_pre, i0 + split_tokens);
-            if (n_win > 0) qpos = P + n_win - 1;
+            if (n_win > 0) qpos = n_pre + n_win - 1;
         } else {
             i0 = n_pre + (split - ns_pre) * split_tokens;
             i1 = min(Tb, i0 + split_tokens);
@@ -187,13 +186,16 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     const T* Kr = (const T*)c.k + head_off + (size_t)c.Pmax * D;
     const T* Vr = (const T*)c.v + head_off + (size_t)c.Pmax * D;
 
-    // Logical entry i -> physical row: the prefix rows, then the filled ring rows.
+    // Logical entry i -> physical row: the prefix rows, then the window's ring rows from
+    // ring_head on, wrapping once. Attention does not depend on the order of its keys, so
+    // a full ring is read from slot 0.
     auto load = [&](Tile& t, int base_i) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = min(base_i + u * KPW + grp, i1 - 1);
             const bool pre = i < n_pre;
-            const size_t row = (size_t)(pre ? i : i - n_pre) * D;
+            const int rr = i - n_pre + ring_head;
+            const size_t row = (size_t)(pre ? i : (rr >= c.W ? rr - c.W : rr)) * D;
             const u32x4* kp = reinterpret_cast<const u32x4*>((pre ? Kp : Kr) + row);
             const u32x4* vp = reinterpret_cast<const u32x4*>((pre ? Vp : Vr) + row);
 #pragma unroll
@@ -351,8 +353,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DevCache c, typename Elem<DT>:
     using T = typename Elem<DT>::T;
     const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int n = len_cur[b];
-    const int P = c.pre[b];
-    const int ns = split_count(min(n, P), min(c.W, max(0, n - P)), split_tokens, c.pe_mode);
+    const SeqView sv = seq_view(c, b, n);
+    const int ns = split_count(sv.n_pre, sv.n_win, split_tokens, c.pe_mode);
     const size_t base = ((size_t)b * c.Hq + hq) * c.max_splits;
     const float* ml = c.part_ml + base * 2;
     float M = -INFINITY;

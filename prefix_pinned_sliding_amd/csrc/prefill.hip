@@ -2,11 +2,12 @@
 // keys.
 //
 // A chunk of C new tokens at positions n .. n + C - 1 of a sequence: query row c (at
-// p = n + c) attends to A(p) ([PS] 03): the pinned prefix, the window [p - W + 1, p] and
-// so the chunk's own tokens up to p. Keys come from three ranges, walked in tiles of
-// BN = 64 positions:
-//   prefix   positions [0, min(n, P)) in the cache's prefix slots,
-//   old ring positions [max(P, p_lo - W + 1), n) in the ring (slot (j - P) mod W),
+// p = n + c) attends to A(p) ([PS] 03): the pinned prefix, the window [p - w + 1, p] and
+// so the chunk's own tokens up to p (w: the sequence's window length). Keys come from three
+// ranges, walked in tiles of BN = 64 positions:
+//   prefix   the cache's prefix slots [0, min(n, npin)),
+//   old ring positions [max(wb, p_lo - w + 1), n) in the ring (slot (j - P_b) mod W), with
+//            wb the oldest window position before the chunk,
 //   chunk    positions [n, p_hi] from the staged rotated keys and the input values,
 // where [p_lo, p_hi] are the positions of the workgroup's rows. A tile is skipped when no
 // row sees any of its keys, computed without masks when every row sees every key, and
@@ -77,12 +78,14 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
     const int p = len_cur[b] + j;
     double sn, cs;
     angle_sincos(p, c.inv_freq[i], &sn, &cs);
-    // RESET: for prefix keys the query sits at its renumbered position min(p, P + W - 1)
+    // RESET: for prefix keys the query sits at its renumbered position, its index in the
+    // list [prefix, window] after it is appended: p inside the prefix, else
+    // P + min(w_b, p + 1 - wfloor) - 1
     const bool reset = c.pe_mode == PSA_PE_RESET;
     double snp = sn, csp = cs;
     if (reset) {
         const int P = c.pre[b];
-        const int pp = p < P ? p : P + min(c.W, p + 1 - P) - 1;
+        const int pp = p < P ? p : P + min(c.wlen[b], p + 1 - c.wfloor[b]) - 1;
         if (pp != p) angle_sincos(pp, c.inv_freq[i], &snp, &csp);
     }
     const size_t tok = (size_t)b * chunk + j;
@@ -171,7 +174,7 @@ struct TileSrc {
     const uint16_t *k_cache, *v_cache, *k_chunk, *v_chunk;
     const uint16_t *k_prefix, *v_prefix;   // own prefix slots or the shared-prefix entry
     size_t chunk_row0;   // b * chunk
-    int n, P, W, Pmax, Hkv, h;
+    int n, P, W, Pmax, Hkv, h;             // P: P_b (ring origin), W: ring slots
 };
 
 // This thread's share of a tile into registers: KLD 16-byte chunks of K rows (lanes along
@@ -297,8 +300,9 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     const int b = bh / c.Hkv;
 
     const int n = len_cur[b];
-    const int P = c.pre[b];
-    const int W = c.W;
+    const int P = c.npin[b];      // pinned entries: positions below it are prefix keys
+    const int W = c.wlen[b];      // this sequence's window length
+    const SeqView sv = seq_view(c, b, n);
     const int c0 = qt * BQ;
     const int p_lo = n + c0;
     const int p_hi = n + min(c0 + BQ, chunk) - 1;   // last valid row position
@@ -338,10 +342,12 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 
     const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
 
-    // Key ranges in position space (see Walk).
-    const int nA = min(n, P);
+    // Key ranges in position space (see Walk). Prefix slot i counts as position i: the
+    // prefix keys come first (i < npin) and every window position is >= npin. Promoted
+    // entries (prefix slots P_b .. npin - 1) are older than every chunk row, so visible.
+    const int nA = sv.n_pre;
     const int hi1 = min(P, p_hi + 1);                  // chunk prefix: [n, hi1) when n < P
-    const int lo2 = n > P ? max(P, p_lo - W + 1) : n;  // ring: [lo2, n) when n > P
+    const int lo2 = max(sv.wb, p_lo - W + 1);          // ring: [lo2, n), empty when n <= wb
     const int lo3 = max(n, P);                         // chunk window: [lo3, p_hi]
     const Walk wk{nA, n, hi1, lo2, n, lo3, p_hi + 1, P, p_lo - W + 1};
     const int pid = c.pid[b];
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
                       (const uint16_t*)c.stage_k, v_in,
                       (const uint16_t*)(pid >= 0 ? c.pool_k : c.k) + pre_off,
                       (const uint16_t*)(pid >= 0 ? c.pool_v : c.v) + pre_off,
-                      (size_t)b * chunk, n, P, W, c.Pmax, c.Hkv, h};
+                      (size_t)b * chunk, n, c.pre[b], c.W, c.Pmax, c.Hkv, h};
 
     u32x4 kreg[KLD], vreg[4];
     int seg = 0, t0 = -kBN;

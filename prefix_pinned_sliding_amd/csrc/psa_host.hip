@@ -41,6 +41,9 @@ struct psa_cache {
     std::vector<int64_t> len;      // host mirror of history lengths
     std::vector<int32_t> pre;      // host mirror of P_b; -1 = never reset
     std::vector<int32_t> pid;      // shared-prefix entry per sequence, -1 = own prefix
+    std::vector<int32_t> npin;     // pinned entries once the prefix is complete
+    std::vector<int32_t> wfloor;   // no window entry is older than this position
+    std::vector<int32_t> wlen;     // window length per sequence
     std::vector<int32_t> pool_len; // tokens held by each pool entry, -1 = never loaded
     std::vector<int32_t> attached; // sequences attached to each pool entry
     int32_t split_tokens;          // 0 = automatic
@@ -94,7 +97,7 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     L->pool_k = off;   off = align_up(off + pool, A);
     L->pool_v = off;   off = align_up(off + pool, A);
     L->tags = off;     off = align_up(off + B * (size_t)S * 4, A);
-    L->state = off;    off = align_up(off + 5 * B * 4, A);
+    L->state = off;    off = align_up(off + 8 * B * 4, A);
     L->inv_freq = off; off = align_up(off + D / 2 * 8, A);
     L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
     L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
@@ -137,14 +140,16 @@ int timed(psa_cache* c, int kernel, hipStream_t s, const char* what, F&& launch)
     return PSA_OK;
 }
 
-// Visible entries of sequence b: min(n, P_b) prefix entries plus min(W, n - P_b) window entries.
+// What sequence b holds now (the same function the kernels evaluate from device state).
+psa::SeqView view_of(const psa_cache* c, int b) {
+    return psa::seq_view((int)c->len[b], c->pre[b], c->npin[b], c->wfloor[b], c->wlen[b],
+                         c->desc.window);
+}
+
+// Visible entries of sequence b: its prefix entries plus its window entries.
 int64_t visible_count(const psa_cache* c, int b) {
-    const int64_t n = c->len[b], P = c->pre[b];
-    const int64_t n_pre = n < P ? n : P;
-    int64_t n_win = n - P;
-    if (n_win < 0) n_win = 0;
-    if (n_win > c->desc.window) n_win = c->desc.window;
-    return n_pre + n_win;
+    const psa::SeqView v = view_of(c, b);
+    return (int64_t)v.n_pre + v.n_win;
 }
 
 // Automatic split length. Split the longest sequence into ns pieces with ns chosen so the
@@ -226,6 +231,9 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     c->len.assign(desc->max_batch, 0);
     c->pre.assign(desc->max_batch, -1);
     c->pid.assign(desc->max_batch, -1);
+    c->npin.assign(desc->max_batch, 0);
+    c->wfloor.assign(desc->max_batch, 0);
+    c->wlen.assign(desc->max_batch, desc->window);
     c->pool_len.assign(desc->n_shared_prefixes, -1);
     c->attached.assign(desc->n_shared_prefixes, 0);
     c->split_tokens = 0;
@@ -248,6 +256,9 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.pre = st + 2 * desc->max_batch;
     d.nnew = st + 3 * desc->max_batch;
     d.pid = st + 4 * desc->max_batch;
+    d.npin = st + 5 * desc->max_batch;
+    d.wfloor = st + 6 * desc->max_batch;
+    d.wlen = st + 7 * desc->max_batch;
     d.inv_freq = (double*)(base + L.inv_freq);
     d.part_o = (float*)(base + L.part_o);
     d.part_ml = (float*)(base + L.part_ml);
@@ -303,6 +314,16 @@ void detach(psa_cache* c, int32_t seq) {
     c->pid[seq] = -1;
 }
 
+// Host mirror of a (re)started sequence with pinned prefix length P (the device side is
+// written by seq_reset_kernel).
+void start(psa_cache* c, int32_t seq, int32_t P, int64_t len) {
+    c->len[seq] = len;
+    c->pre[seq] = P;
+    c->npin[seq] = P;
+    c->wfloor[seq] = P;
+    c->wlen[seq] = c->desc.window;
+}
+
 }  // namespace
 
 PSA_API int psa_seq_reset(psa_cache* c, int32_t seq, int32_t prefix_len, psa_stream stream) {
@@ -314,8 +335,7 @@ PSA_API int psa_seq_reset(psa_cache* c, int32_t seq, int32_t prefix_len, psa_str
         psa::launch_seq_reset(c->dev, seq, prefix_len, 0, -1, c->cur, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sequence reset");
     detach(c, seq);
-    c->len[seq] = 0;
-    c->pre[seq] = prefix_len;
+    start(c, seq, prefix_len, 0);
     return PSA_OK;
 }
 
@@ -348,8 +368,58 @@ PSA_API int psa_seq_attach(psa_cache* c, int32_t seq, int32_t prefix_id, psa_str
     detach(c, seq);
     c->pid[seq] = prefix_id;
     c->attached[prefix_id] += 1;
-    c->len[seq] = P;
-    c->pre[seq] = P;
+    start(c, seq, P, P);
+    return PSA_OK;
+}
+
+PSA_API int psa_seq_set_window(psa_cache* c, int32_t seq, int32_t window, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    if (c->pre[seq] < 0) return fail(PSA_ERR_STATE, "sequence was never reset");
+    if (window < 1 || window > c->desc.window)
+        return fail(PSA_ERR_ARG, "window must be in [1, desc.window]");
+    const psa::SeqView v = view_of(c, seq);
+    const int64_t n = c->len[seq];
+    // entries beyond the new length leave now: the window becomes [wb', n)
+    const int64_t wb1 = n - window > v.wb ? n - window : v.wb;
+    const int lo = v.wb, hi = (int)(wb1 < n ? wb1 : n);
+    const hipError_t e = psa::launch_seq_window(c->dev, seq, window, (int)wb1, lo, hi > lo ? hi : lo,
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "window change");
+    c->wfloor[seq] = (int32_t)wb1;
+    c->wlen[seq] = window;
+    return PSA_OK;
+}
+
+PSA_API int psa_seq_promote(psa_cache* c, int32_t seq, int32_t count, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    if (c->pre[seq] < 0) return fail(PSA_ERR_STATE, "sequence was never reset");
+    if (c->pid[seq] >= 0) return fail(PSA_ERR_STATE, "sequence reads a shared prefix");
+    if (c->desc.pe_mode != PSA_PE_CONTINUE)
+        return fail(PSA_ERR_STATE, "promotion needs PSA_PE_CONTINUE");
+    const psa::SeqView v = view_of(c, seq);
+    if (count < 0 || count > v.n_win) return fail(PSA_ERR_ARG, "count must be in [0, window entries]");
+    if ((int64_t)c->npin[seq] + count > c->desc.prefix_max)
+        return fail(PSA_ERR_ARG, "pinned entries would exceed prefix_max");
+    if (count == 0) return PSA_OK;
+    const hipError_t e =
+        psa::launch_promote(c->dev, seq, v.wb, count, c->npin[seq], (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "promotion");
+    c->npin[seq] += count;
+    c->wfloor[seq] = v.wb + count;
+    return PSA_OK;
+}
+
+PSA_API int psa_seq_window(const psa_cache* c, int32_t seq, int32_t* window, int32_t* pinned,
+                           int32_t* window_entries) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    if (c->pre[seq] < 0) return fail(PSA_ERR_STATE, "sequence was never reset");
+    const psa::SeqView v = view_of(c, seq);
+    if (window) *window = c->wlen[seq];
+    if (pinned) *pinned = v.n_pre;
+    if (window_entries) *window_entries = v.n_win;
     return PSA_OK;
 }
 
@@ -396,9 +466,8 @@ PSA_API int psa_decode_attn(psa_cache* c, const void* q, void* out, float* lse, 
     const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
     int64_t max_ns = 1;
     for (int b = 0; b < B; ++b) {
-        const int64_t n_pre = c->len[b] < c->pre[b] ? c->len[b] : c->pre[b];
-        const int64_t ns =
-            psa::split_count((int)n_pre, (int)(visible_count(c, b) - n_pre), L, c->desc.pe_mode);
+        const psa::SeqView v = view_of(c, b);
+        const int64_t ns = psa::split_count(v.n_pre, v.n_win, L, c->desc.pe_mode);
         if (ns > max_ns) max_ns = ns;
     }
     hipStream_t s = (hipStream_t)stream;
@@ -448,11 +517,11 @@ PSA_API int psa_export(psa_cache* c, int32_t seq, void* k_host, void* v_host, in
     if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
     if (c->pre[seq] < 0) return fail(PSA_ERR_STATE, "export of a sequence that was never reset");
     const psa::DevCache& d = c->dev;
-    const int64_t n = c->len[seq], P = c->pre[seq], W = d.W;
-    const int64_t n_pre = n < P ? n : P;
+    const psa::SeqView sv = view_of(c, seq);
+    const int64_t W = d.W;
+    const int64_t n_pre = sv.n_pre;
     const int64_t cnt = visible_count(c, seq);
-    const int64_t base = (n - W > P) ? n - W : P;   // oldest window position
-    const int64_t head = (base - P) % W;             // ring slot holding it
+    const int64_t head = (sv.wb - c->pre[seq]) % W;  // ring slot holding the oldest entry
     const size_t elem = (size_t)c->L.elem, D = (size_t)d.D, S = (size_t)d.S, Hkv = (size_t)d.Hkv;
     const size_t row = D * elem;
     const size_t seq_bytes = Hkv * S * row;

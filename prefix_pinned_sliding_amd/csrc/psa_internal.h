@@ -23,12 +23,16 @@ struct DevCache {
     int32_t* pre;        // [B] prefix length P_b
     int32_t* nnew;       // [B] per-call token counts (ragged append)
     int32_t* pid;        // [B] shared-prefix entry of each sequence, -1 for its own prefix
+    int32_t* npin;       // [B] pinned entries once the prefix is complete (P_b + promoted)
+    int32_t* wfloor;     // [B] no window entry is older than this position
+    int32_t* wlen;       // [B] the sequence's window length w_b (<= W)
     double* inv_freq;    // [D/2] theta_i
     float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
     void* stage_k;       // [B][max_chunk][Hkv][D] rotated prefill-chunk keys (stored bytes)
     void* stage_q;       // [B][max_chunk][Hq][D] rotated, scaled prefill-chunk queries (bf16)
     void* stage_qp;      // same, rotated at the renumbered position for prefix keys (RESET)
+    // W: ring slots per (sequence, head), the largest window any sequence may use
     int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits, n_shared, shared_max, pe_mode;
     float scale;
 };
@@ -41,11 +45,42 @@ struct Layout {
 
 bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why);
 
+// What sequence b holds when its history has n tokens. Positions p < P_b fill prefix slot
+// p; every later position p sits in ring slot (p - P_b) mod W. The window is the position
+// range [wb, n) with wb = max(wfloor, n - w_b): appends move it by the length rule alone,
+// while a window change or a promotion raises wfloor. Promoted entries occupy prefix
+// slots P_b .. npin - 1, and every window position is >= npin.
+struct SeqView {
+    int n_pre;   // prefix slots in use: min(n, npin)
+    int wb;      // oldest window position
+    int n_win;   // window entries, max(0, n - wb)
+    int head;    // ring slot of the oldest window entry (0 when all W slots are live)
+};
+
+__host__ __device__ inline SeqView seq_view(int n, int P, int npin, int wfloor, int wlen, int W) {
+    SeqView v;
+    v.n_pre = n < npin ? n : npin;
+    v.wb = n - wlen > wfloor ? n - wlen : wfloor;
+    v.n_win = n > v.wb ? n - v.wb : 0;
+    v.head = v.n_win == W ? 0 : (v.wb - P) % W;
+    return v;
+}
+
+__device__ inline SeqView seq_view(const DevCache& c, int b, int n) {
+    return seq_view(n, c.pre[b], c.npin[b], c.wfloor[b], c.wlen[b], c.W);
+}
+
 // Kernel launchers (stream-ordered, asynchronous). They return the launch status.
 hipError_t launch_init(const DevCache& c, hipStream_t s);
 // Start a sequence: tags -1, length `len0`, prefix length `prefix_len`, prefix entry `pid`.
 hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int len0, int pid, int cur,
                             hipStream_t s);
+// Set a sequence's window length and floor; clear the tags of ring positions [clr_lo, clr_hi).
+hipError_t launch_seq_window(const DevCache& c, int seq, int wlen, int wfloor, int clr_lo,
+                             int clr_hi, hipStream_t s);
+// Move window positions [wb, wb + count) of sequence seq from their ring slots to prefix
+// slots npin .. npin + count - 1, then npin += count and wfloor = wb + count.
+hipError_t launch_promote(const DevCache& c, int seq, int wb, int count, int npin, hipStream_t s);
 // Rotate and store `len` prefix tokens (k, v: [len][Hkv][D]) into pool entry `id`.
 hipError_t launch_pool_load(const DevCache& c, int id, int len, const void* k, const void* v,
                             hipStream_t s);

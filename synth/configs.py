@@ -1,4 +1,4 @@
-"""The five synthetic workloads the path is tested and measured on.
+"""The synthetic workloads the path is tested and measured on.
 
 Shapes only, plus the seeded per-sequence draws of prefix lengths and start
 positions. "At t" is the 1-based position of the first new token, so the
@@ -34,6 +34,7 @@ class Workload:
     chunk: int = 0             # prefill chunk length
     rope_base: float = 10000.0
     seed: int = 0
+    windows: Optional[List[int]] = None   # per-sequence window lengths (None: all `window`)
 
     @property
     def prefix_max(self) -> int:
@@ -43,9 +44,12 @@ class Workload:
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.head_dim)
 
+    def window_of(self, b: int) -> int:
+        return self.window if self.windows is None else self.windows[b]
+
     def visible_tokens(self, n: List[int]) -> int:
-        """Sum over sequences of the visible count min(n_b, P_b + W) for history lengths n."""
-        return sum(min(nb, pb + self.window) for nb, pb in zip(n, self.prefix))
+        """Sum over sequences of the visible count min(n_b, P_b + w_b) for history lengths n."""
+        return sum(min(nb, pb + self.window_of(b)) for b, (nb, pb) in enumerate(zip(n, self.prefix)))
 
 
 def tiny_fp32(seed: int = 0) -> Workload:
@@ -91,6 +95,16 @@ def decode_shared_p2000(seed: int = 0, batch: int = 64, t: int = 32768) -> Workl
                     128, 4096, [2000] * batch, [t] * batch, "decode", steps=1, seed=seed)
 
 
+def decode_ragged_window(seed: int = 0, batch: int = 64, t: int = 32768) -> Workload:
+    """bf16, 64 sequences at t=32768, 16/8 heads, D=128, P=100, ring of 4096 slots and a
+    window length per sequence w_b ~ U{256..4096}."""
+    rng = np.random.Generator(np.random.PCG64(seed + 11))
+    wins = [int(x) for x in rng.integers(256, 4096, size=batch, endpoint=True)]
+    return Workload(f"decode-bf16-B{batch}-P100-Wragged256to4096-t{t}", torch.bfloat16, batch, 16,
+                    8, 128, 4096, [100] * batch, [t] * batch, "decode", steps=1, seed=seed,
+                    windows=wins)
+
+
 ALL = {
     "tiny_fp32": tiny_fp32,
     "decode_p100_w4096": decode_p100_w4096,
@@ -98,6 +112,7 @@ ALL = {
     "decode_p512_w16384": decode_p512_w16384,
     "ragged_decode": ragged_decode,
     "decode_shared_p2000": decode_shared_p2000,
+    "decode_ragged_window": decode_ragged_window,
 }
 
 

@@ -98,6 +98,8 @@ def fill(cache, wl: Workload, n_hist: List[int], device="cuda", chunk: Optional[
     if reset:
         for b in range(B):
             cache.reset(b, wl.prefix[b])
+            if wl.windows is not None:
+                cache.set_window(b, wl.windows[b])
     maxn = max(n_hist) if n_hist else 0
     if chunk is None:
         per_pos = B * wl.n_kv_heads * wl.head_dim
