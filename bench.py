@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-calls", type=int, default=10)
+    ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--train-calls", type=int, default=5)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB with torch (counter calibration)")
     return ap.parse_args()
@@ -175,6 +177,59 @@ def bench_prefill(calls: int, warmup: int = 2):
             "kernels_avg_us": {k: (ms / n * 1e3 if n else None) for k, (ms, n) in times.items()}}
 
 
+def bench_train(calls: int, warmup: int = 2):
+    """Training attention on the truncated back-propagation shape of the pages: a 100-token
+    prompt plus 4W = 16384 lead tokens with W = 4096, 4 sequences, 16/8 heads, D = 128.
+
+    Forward writes out and lse; backward computes dq, dk, dv from them. Algorithmic flops
+    (the FlashAttention convention): forward 2 products, backward 5 (S recomputed, dP, dV,
+    dK, dQ), each 2 * H_q * D * sum over rows of |A(row)| flops. Timed with events on the
+    stream the kernels are launched on (torch's current stream).
+    """
+    import torch
+
+    import prefix_pinned_sliding_amd as psa
+    from synth import gen
+
+    B, W, P, Hq, Hkv, D = 4, 4096, 100, 16, 8, 128
+    T = P + 4 * W
+
+    def draw(stream, H):
+        return gen.normal_block(0, stream, list(range(B)), [0] * B, T, H, D, torch.bfloat16, "cuda")
+
+    q, k, v, g = draw(gen.STREAM_Q, Hq), draw(gen.STREAM_K, Hkv), draw(gen.STREAM_V, Hkv), \
+        draw(gen.STREAM_DO, Hq)
+    ta = psa.TrainAttention(B, T, Hq, Hkv, D, W)
+    pre = [P] * B
+    out, lse = ta.forward(q, k, v, pre)
+    dq, dk, dv = ta.backward(q, k, v, out, lse, g, pre)
+    for _ in range(warmup):
+        ta.forward(q, k, v, pre, out=out, lse=lse)
+        ta.backward(q, k, v, out, lse, g, pre, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(calls):
+        ta.forward(q, k, v, pre, out=out, lse=lse)
+    ev[1].record()
+    for _ in range(calls):
+        ta.backward(q, k, v, out, lse, g, pre, dq=dq, dk=dk, dv=dv)
+    ev[2].record()
+    torch.cuda.synchronize()
+    fwd_s = ev[0].elapsed_time(ev[1]) / calls / 1e3
+    bwd_s = ev[1].elapsed_time(ev[2]) / calls / 1e3
+    pairs = sum(i + 1 if i < P else P + min(W, i - P + 1) for i in range(T)) * B
+    unit = 2.0 * Hq * D * pairs
+    fwd_tf, bwd_tf = 2 * unit / fwd_s / 1e12, 5 * unit / bwd_s / 1e12
+    return {"workload": f"train-bf16-B{B}-P{P}-W{W}-T{T}", "calls": calls,
+            "fwd_ms": fwd_s * 1e3, "bwd_ms": bwd_s * 1e3,
+            "tokens_per_s_fwd_bwd": B * T / (fwd_s + bwd_s),
+            "fwd_tflops": fwd_tf,
+            "roofline": {"bound": "mfma", "achieved": bwd_tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": bwd_tf / MFMA_BF16_PEAK_TFLOPS,
+                         "kernel": "backward (rowdot + dkdv + dq)", "flops_per_launch": 5 * unit}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +352,11 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] chunked prefill", file=sys.stderr, flush=True)
         result["prefill"] = bench_prefill(args.prefill_calls)
+
+    if not args.no_train and args.workload == "decode_p100_w4096":
+        torch.cuda.empty_cache()
+        print("[bench] training attention", file=sys.stderr, flush=True)
+        result["train"] = bench_train(args.train_calls)
 
     if not args.no_cpu_baseline:
         qc = qs[total - 1].double().cpu().numpy()

@@ -234,6 +234,49 @@ int psa_prefill_attn(psa_cache *cache, int32_t chunk, const void *q, const void 
 int psa_export(psa_cache *cache, int32_t seq, void *k_host, void *v_host, int32_t *pos_host,
                int32_t *count, psa_stream stream);
 
+/* Training attention over the same visible set ([PS] 08: chunked or truncated
+ * back-propagation through long traces needs the gradient of the generator's attention).
+ * Works on caller tensors, not on a cache. A segment of sequence b has len_b rows: rows
+ * [0, P_b) are its pinned prefix, later rows consecutive positions (for truncated
+ * back-propagation, the prompt followed by the last tokens of the trace). Key row j is
+ * visible to query row i iff j <= i and (j < P_b or j >= i - W + 1), the set A(t) of
+ * [PS] 03 in row indices. Queries and keys are passed already rotated at their positions
+ * (the rotation and its transpose in the backward pass are the caller's), so the calls
+ * compute out = softmax(scale * q k^T + mask) v and its gradients.
+ * Tensors are bf16 and dense: q, out, dout, dq: [B][T][H_q][D]; k, v, dk, dv:
+ * [B][T][H_kv][D]; lse: [B][T][H_q] float32, natural log. Rows >= len_b are neither read
+ * nor written. prefix_host, len_host: host arrays of B entries (len_host NULL: all T);
+ * 0 <= P_b, 1 <= len_b <= T. workspace: caller-owned device memory of
+ * psa_train_workspace_bytes() bytes, 256-byte aligned. Errors: PSA_ERR_ARG for a null
+ * pointer, unsupported shape, a length or prefix out of range, or a short workspace. */
+typedef struct {
+    int32_t batch;       /* B >= 1 */
+    int32_t seq_len;     /* T >= 1: rows per sequence (tensor stride) */
+    int32_t n_q_heads;   /* H_q, a multiple of n_kv_heads with H_q / H_kv in {1, 2, 4, 8} */
+    int32_t n_kv_heads;  /* H_kv >= 1 */
+    int32_t head_dim;    /* D: 64 or 128 */
+    int32_t window;      /* W >= 1 */
+    float scale;         /* softmax scale; 0 selects 1 / sqrt(head_dim) */
+    int32_t reserved;    /* must be 0 */
+} psa_train_desc;
+
+/* Workspace bytes for psa_train_fwd / psa_train_bwd (0 for an invalid description). */
+size_t psa_train_workspace_bytes(const psa_train_desc *desc);
+
+/* Forward: writes out and lse. */
+int psa_train_fwd(const psa_train_desc *desc, const int32_t *prefix_host,
+                  const int32_t *len_host, const void *q, const void *k, const void *v,
+                  void *out, float *lse, void *workspace, size_t workspace_bytes,
+                  psa_stream stream);
+
+/* Backward: given the forward's out and lse and dout = dL/dout, writes dq = dL/dq,
+ * dk = dL/dk and dv = dL/dv (a KV head's gradient sums over the query heads that read
+ * it). */
+int psa_train_bwd(const psa_train_desc *desc, const int32_t *prefix_host,
+                  const int32_t *len_host, const void *q, const void *k, const void *v,
+                  const void *out, const float *lse, const void *dout, void *dq, void *dk,
+                  void *dv, void *workspace, size_t workspace_bytes, psa_stream stream);
+
 /* History length of `seq` from the host mirror (-1 if seq is out of range or the
  * sequence was never reset). Host only. */
 int64_t psa_seq_length(const psa_cache *cache, int32_t seq);

@@ -63,6 +63,19 @@ class Layout(ctypes.Structure):
     ]
 
 
+class TrainDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -90,6 +103,10 @@ def _load() -> ctypes.CDLL:
         "psa_profile": (ctypes.c_int, [P, I32]),
         "psa_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(I64)]),
+        "psa_train_workspace_bytes": (SZ, [ctypes.POINTER(TrainDesc)]),
+        "psa_train_fwd": (ctypes.c_int, [ctypes.POINTER(TrainDesc), P, P, P, P, P, P, P, P, SZ, P]),
+        "psa_train_bwd": (ctypes.c_int, [ctypes.POINTER(TrainDesc), P, P, P, P, P, P, P, P, P, P,
+                                         P, P, SZ, P]),
         "psa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "psa_last_error": (ctypes.c_char_p, []),
     }
@@ -314,3 +331,60 @@ class Cache:
         _check(lib.psa_profile_read(self._h, kernel, ctypes.byref(ms), ctypes.byref(n)),
                "psa_profile_read")
         return ms.value, n.value
+
+
+class TrainAttention:
+    """Masked attention forward and backward on caller tensors (bf16, row space).
+
+    q, out, dout, dq: [B][T][H_q][D]; k, v, dk, dv: [B][T][H_kv][D]; lse [B][T][H_q] float32.
+    prefix[b] rows are the pinned prefix of sequence b; lens[b] its valid rows (default T).
+    """
+
+    def __init__(self, batch: int, seq_len: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 window: int, scale: float = 0.0, device="cuda"):
+        self.desc = TrainDesc(batch, seq_len, n_q_heads, n_kv_heads, head_dim, window, scale, 0)
+        nb = lib.psa_train_workspace_bytes(ctypes.byref(self.desc))
+        if nb == 0:
+            raise PsaError(PSA_ERR_ARG, "psa_train_workspace_bytes")
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+        self.B, self.T, self.Hq, self.Hkv, self.D = batch, seq_len, n_q_heads, n_kv_heads, head_dim
+
+    def _seq(self, prefix, lens):
+        if len(prefix) != self.B or (lens is not None and len(lens) != self.B):
+            raise ValueError("prefix and lens need one entry per sequence")
+        pre = (ctypes.c_int32 * self.B)(*[int(x) for x in prefix])
+        ln = None if lens is None else (ctypes.c_int32 * self.B)(*[int(x) for x in lens])
+        return pre, ln
+
+    def _check(self, t: torch.Tensor, name: str, heads: int, dtype=torch.bfloat16) -> None:
+        want = (self.B, self.T, heads) + (() if dtype == torch.float32 else (self.D,))
+        if t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != want or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor of shape {want}")
+
+    def forward(self, q, k, v, prefix, lens=None, out=None, lse=None, stream=None):
+        for name, t, hh in (("q", q, self.Hq), ("k", k, self.Hkv), ("v", v, self.Hkv)):
+            self._check(t, name, hh)
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+        self._check(out, "out", self.Hq)
+        self._check(lse, "lse", self.Hq, torch.float32)
+        pre, ln = self._seq(prefix, lens)
+        _check(lib.psa_train_fwd(ctypes.byref(self.desc), pre, ln, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(out), _ptr(lse), _ptr(self.ws), self.ws.numel(),
+                                 _stream(stream)), "psa_train_fwd")
+        return out, lse
+
+    def backward(self, q, k, v, out, lse, dout, prefix, lens=None, dq=None, dk=None, dv=None,
+                 stream=None):
+        for name, t, hh in (("q", q, self.Hq), ("k", k, self.Hkv), ("v", v, self.Hkv),
+                            ("out", out, self.Hq), ("dout", dout, self.Hq)):
+            self._check(t, name, hh)
+        self._check(lse, "lse", self.Hq, torch.float32)
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        pre, ln = self._seq(prefix, lens)
+        _check(lib.psa_train_bwd(ctypes.byref(self.desc), pre, ln, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(self.ws), self.ws.numel(), _stream(stream)), "psa_train_bwd")
+        return dq, dk, dv

@@ -25,16 +25,12 @@
 // folded into the staged queries; the running max is raised only when a tile exceeds it
 // by more than 2^8.
 #include "psa_internal.h"
+#include "mfma_tile.h"
 #include "rope_round.h"
 
 namespace psa {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 #ifndef PSA_PREFILL_PIPELINE
 #define PSA_PREFILL_PIPELINE 1   // 1: fetch the next tile's K/V while computing this one
@@ -44,11 +40,6 @@ constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kRows = 128;              // rows (position x head) per workgroup
 constexpr int kBN = 64;                 // keys per tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNeg = -1.0e30f;        // initial running max (finite: -inf - kNeg = -inf)
-__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-constexpr float kRescaleSlack = 8.0f;
 
 // float64 -> bfloat16 for staged queries: the same single rounding as stored keys.
 __device__ __forceinline__ uint16_t q_to_bf16(double x) { return f64_to_bf16_bits(x); }
@@ -118,21 +109,6 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
     }
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-// Max over lanes l, l^16, l^32, l^48 (the four lane groups holding one row).
-__device__ __forceinline__ float row_max4(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
-}
-__device__ __forceinline__ float row_sum4(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-}
 
 // The key ranges of a workgroup, in walk order: 0 = prefix in the cache, 1 = prefix
 // tokens inside the chunk (n < P), 2 = still-visible ring (n > P), 3 = window tokens of
@@ -228,14 +204,6 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
     }
 }
 
-// V^T column of the first of 4 keys 4kq .. 4kq + 3. Within each 32-key group, lane group g
-// of an MFMA k-step needs keys 4g .. 4g+3 and 16 + 4g .. 16 + 4g + 3 (the accumulator
-// layout of S^T); storing those 8 keys side by side at columns 8g .. 8g + 7 turns the
-// operand into one aligned 16-byte LDS read.
-__device__ __forceinline__ int vt_col(int kq) {
-    const int q = kq & 7;
-    return 32 * (kq >> 3) + (q < 4 ? 8 * q : 8 * (q - 4) + 4);
-}
 
 // Registers -> LDS: K rows as they are, V transposed (4 keys x 8 dims -> 8 rows of V^T
 // holding 4 keys each, columns permuted by vt_col).
@@ -251,21 +219,7 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int ti
         *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
     }
     const int kq = tid % (BN / 4), dc = tid / (BN / 4);
-    if (dc < CPR) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t a0 = vreg[0][x], a1 = vreg[1][x], a2 = vreg[2][x], a3 = vreg[3][x];
-            u32x2 lo, hi;   // dims 2x (low halves) and 2x + 1 (high halves)
-            lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-            lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-            hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-            hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-            const int d0 = dc * 8 + 2 * x;
-            const int col = vt_col(kq);
-            *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + col) = lo;
-            *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + col) = hi;
-        }
-    }
+    if (dc < CPR) store_transposed4<VSTR>(vt_s, kq, dc, vreg);
 }
 
 template <int D, int G>

@@ -637,6 +637,119 @@ PSA_API int psa_profile_read(psa_cache* c, int32_t kernel, double* total_ms, int
     return PSA_OK;
 }
 
+namespace {
+
+struct TrainWs {
+    size_t info, di, total;
+};
+
+bool train_check(const psa_train_desc* d, TrainWs* ws, const char** why) {
+    auto bad = [&](const char* w) {
+        *why = w;
+        return false;
+    };
+    if (d == nullptr) return bad("desc is NULL");
+    if (d->batch < 1 || d->seq_len < 1) return bad("batch and seq_len must be >= 1");
+    if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
+        return bad("n_q_heads must be a positive multiple of n_kv_heads");
+    const int G = d->n_q_heads / d->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return bad("n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+    if (d->head_dim != 64 && d->head_dim != 128) return bad("head_dim must be 64 or 128");
+    if (d->window < 1) return bad("window must be >= 1");
+    if (!(d->scale >= 0.f) || !isfinite(d->scale)) return bad("scale must be finite and >= 0");
+    if (d->reserved != 0) return bad("reserved must be 0");
+    const size_t rows = (size_t)d->batch * d->seq_len * d->n_q_heads;
+    if ((size_t)d->batch * d->seq_len > (size_t)1 << 31) return bad("batch * seq_len too large");
+    ws->info = 0;
+    ws->di = align_up(2 * (size_t)d->batch * 4, 256);
+    ws->total = align_up(ws->di + rows * 4, 256);
+    return true;
+}
+
+int train_run(const psa_train_desc* d, const int32_t* prefix_host, const int32_t* len_host,
+              const void* q, const void* k, const void* v, const void* out_in, void* out,
+              float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+              size_t ws_bytes, psa_stream stream, bool backward) {
+    TrainWs ws;
+    const char* why = nullptr;
+    if (!train_check(d, &ws, &why)) return fail(PSA_ERR_ARG, why);
+    if (prefix_host == nullptr) return fail(PSA_ERR_ARG, "prefix_host is NULL");
+    if (workspace == nullptr || ws_bytes < ws.total)
+        return fail(PSA_ERR_ARG, "workspace missing or smaller than psa_train_workspace_bytes()");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(PSA_ERR_ARG, "workspace must be 256-byte aligned");
+    const int B = d->batch;
+    std::vector<int32_t> info(2 * (size_t)B);
+    for (int b = 0; b < B; ++b) {
+        const int32_t n = len_host ? len_host[b] : d->seq_len;
+        if (n < 1 || n > d->seq_len) return fail(PSA_ERR_ARG, "len must be in [1, seq_len]");
+        if (prefix_host[b] < 0) return fail(PSA_ERR_ARG, "prefix lengths must be >= 0");
+        info[b] = prefix_host[b];
+        info[B + b] = n;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)workspace;
+    hipError_t e = hipMemcpyAsync(w + ws.info, info.data(), info.size() * sizeof(int32_t),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "sequence-info upload");
+    psa::TrainLaunch t;
+    t.q = q;
+    t.k = k;
+    t.v = v;
+    t.dout = dout;
+    t.out = backward ? const_cast<void*>(out_in) : out;
+    t.dq = dq;
+    t.dk = dk;
+    t.dv = dv;
+    t.lse = lse;
+    t.di = (float*)(w + ws.di);
+    t.pre = (const int32_t*)(w + ws.info);
+    t.len = t.pre + B;
+    t.B = B;
+    t.T = d->seq_len;
+    t.Hq = d->n_q_heads;
+    t.Hkv = d->n_kv_heads;
+    t.D = d->head_dim;
+    t.W = d->window;
+    t.scale = d->scale > 0.f ? d->scale : (float)(1.0 / sqrt((double)d->head_dim));
+    t.backward = backward;
+    e = psa::launch_train(t, s);
+    if (e != hipSuccess) return hip_fail(e, backward ? "training backward" : "training forward");
+    return PSA_OK;
+}
+
+}  // namespace
+
+PSA_API size_t psa_train_workspace_bytes(const psa_train_desc* desc) {
+    TrainWs ws;
+    const char* why = nullptr;
+    if (!train_check(desc, &ws, &why)) {
+        fail(PSA_ERR_ARG, why);
+        return 0;
+    }
+    return ws.total;
+}
+
+PSA_API int psa_train_fwd(const psa_train_desc* desc, const int32_t* prefix_host,
+                          const int32_t* len_host, const void* q, const void* k, const void* v,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          psa_stream stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr)
+        return fail(PSA_ERR_ARG, "q, k, v, out or lse is NULL");
+    return train_run(desc, prefix_host, len_host, q, k, v, nullptr, out, lse, nullptr, nullptr,
+                     nullptr, nullptr, workspace, workspace_bytes, stream, false);
+}
+
+PSA_API int psa_train_bwd(const psa_train_desc* desc, const int32_t* prefix_host,
+                          const int32_t* len_host, const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                          void* dv, void* workspace, size_t workspace_bytes, psa_stream stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr ||
+        dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+        return fail(PSA_ERR_ARG, "an input or output pointer is NULL");
+    return train_run(desc, prefix_host, len_host, q, k, v, out, nullptr, const_cast<float*>(lse),
+                     dout, dq, dk, dv, workspace, workspace_bytes, stream, true);
+}
+
 PSA_API const char* psa_status_string(int status) {
     switch (status) {
         case PSA_OK: return "ok";

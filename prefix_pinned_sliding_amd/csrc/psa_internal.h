@@ -109,4 +109,17 @@ hipError_t launch_prefill_stage(const DevCache& c, const void* q, const void* k,
 hipError_t launch_prefill(const DevCache& c, const void* v, void* out, float* lse, int chunk,
                           int cur, hipStream_t s);
 
+// Training attention (row space): forward writes out and lse; backward reads q, k, v,
+// out, lse, dout and writes dq, dk, dv (di: float32 workspace [B][T][Hq]).
+struct TrainLaunch {
+    const void *q, *k, *v, *dout;
+    void *out, *dq, *dk, *dv;
+    float *lse, *di;
+    const int32_t *pre, *len;   // device [B]
+    int B, T, Hq, Hkv, D, W;
+    float scale;
+    bool backward;
+};
+hipError_t launch_train(const TrainLaunch& t, hipStream_t s);
+
 }  // namespace psa

@@ -1,0 +1,593 @@
+// Attention forward and backward over the prefix-window mask for training, on MFMA.
+//
+// [PS] 08: the trainer back-propagates long traces chunk by chunk, or only through the last
+// window with a few windows of lead context; either way the attention it differentiates is
+// the generator's: key row j is visible to query row i iff j <= i and (j < P or
+// j >= i - W + 1), rows [0, P) being the pinned prefix and later rows consecutive
+// positions. Queries and keys arrive rotated, so this is masked attention in row space.
+//
+// Forward: out and lse (natural log) per (row, query head), the prefill kernel's scheme
+// (S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, 128 rows = 128 / G
+// positions x G heads per workgroup, 64-key tiles, skipped / unmasked / masked tiles).
+// Backward, three kernels:
+//   rowdot  Di = sum_d dO * O per (row, head) (float32);
+//   dkdv    one workgroup per 64-key tile; each wave keeps its 16 keys' K and V in registers
+//           and walks the query tiles that see the tile: S = Q K^T, dP = dO V^T,
+//           P = exp(S - lse), dS = P (dP - Di), dV += P^T dO, dK += dS^T Q;
+//   dq      one workgroup per 128-row query tile walking its visible key tiles:
+//           S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+// P and dS enter the second products as bf16, accumulation is float32 throughout.
+#include "mfma_tile.h"
+#include "psa_internal.h"
+
+namespace psa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBlock = 64 * kWaves;
+constexpr int kRows = 128;   // query rows per forward / dq workgroup
+constexpr int kBN = 64;      // keys per tile
+constexpr int kBR = 64;      // query rows per dkdv step
+
+struct TrainArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    uint16_t *out, *dq, *dk, *dv;
+    float* lse;              // [B][T][Hq] natural log
+    float* di;               // [B][T][Hq] workspace: sum_d dO * O
+    const int32_t* pre;      // [B] prefix rows
+    const int32_t* len;      // [B] valid rows
+    int B, T, Hq, Hkv, W;
+    float scale;
+};
+
+__device__ __forceinline__ bool visible(int i, int j, int P, int W) {
+    return j <= i && (j < P || j >= i - W + 1);
+}
+
+// XCD-aware order: workgroup L runs on XCD L % 8; consecutive logical tiles (those of one
+// (sequence, KV head)) go to one XCD so the operands they share stay in its L2.
+__device__ __forceinline__ int xcd_logical(int total) {
+    const int per_xcd = (total + 7) / 8;
+    const int L = blockIdx.x;
+    return (L % 8) * per_xcd + L / 8;
+}
+
+// The two key ranges of query rows [r_lo, r_hi]: prefix [0, min(P, r_hi + 1)) and band
+// [max(P, r_lo - W + 1), r_hi + 1). walk() steps (seg, t0) through them in 64-key tiles.
+struct KeyWalk {
+    int hi0, lo1, hi1;
+    __device__ bool next(int& seg, int& t0) const {
+        t0 += kBN;
+        if (seg == 0 && t0 >= hi0) {
+            seg = 1;
+            t0 = lo1;
+        }
+        return seg == 0 || t0 < hi1;
+    }
+};
+
+// Row-major copy of 4 rows x 16 bytes per thread: rows 4kq .. 4kq + 3, chunk dc, with row
+// r at src + off(r) (off: element offset), rows beyond `last` reading row `last`.
+template <typename Off>
+__device__ __forceinline__ void load4(const uint16_t* src, int kq, int dc, int last, Off off,
+                                      u32x4* r) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        r[x] = *reinterpret_cast<const u32x4*>(src + off(min(4 * kq + x, last)) + dc * 8);
+}
+
+template <int STR>
+__device__ __forceinline__ void store_rows4(uint16_t* dst, int kq, int dc, const u32x4* r) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        *reinterpret_cast<u32x4*>(dst + (4 * kq + x) * STR + dc * 8) = r[x];
+}
+
+// ---------------------------------------------------------------------------------------
+// Forward.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n_qtiles) {
+    constexpr int BQ = kRows / G;
+    constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
+    constexpr int KSTR = D + 8, VSTR = kBN + 8, CPR = D / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
+
+    const int total = n_qtiles * a.Hkv * a.B;
+    const int logical = xcd_logical(total);
+    if (logical >= total) return;
+    const int qt = logical % n_qtiles, bh = logical / n_qtiles;
+    const int h = bh % a.Hkv, b = bh / a.Hkv;
+    const int len = a.len[b], P = a.pre[b], W = a.W;
+    const int c0 = qt * BQ;
+    if (c0 >= len) return;
+    const int p_lo = c0, p_hi = min(c0 + BQ, len) - 1;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const float sc = a.scale * kLog2e;
+
+    int row_pos[2];
+    bf16x8 qop[2][KS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = 32 * wave + 16 * rb + l16;
+        row_pos[rb] = c0 + r / G;
+        const int cl = min(row_pos[rb], len - 1);
+        const size_t off = (((size_t)b * a.T + cl) * a.Hq + h * G + r % G) * D + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.q + off + ks * 32));
+    }
+    f32x4 o[2][DB];
+    float m[2] = {kNeg, kNeg}, lp[2] = {0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const KeyWalk wk{min(P, p_hi + 1), max(P, p_lo - W + 1), p_hi + 1};
+    const size_t kv0 = (size_t)b * a.T * a.Hkv + h;   // row j at (kv0 + j * Hkv) * D
+    const int kq = tid % (kBN / 4), dc = tid / (kBN / 4);
+    int seg = 0, t0 = -kBN;
+#pragma unroll 1
+    while (wk.next(seg, t0)) {
+        const int t1 = min(t0 + kBN, seg == 0 ? wk.hi0 : wk.hi1);
+        const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) && (t1 - 1 < P || t0 >= p_hi - W + 1);
+        __syncthreads();
+        if (dc < CPR) {
+            auto off = [&](int r) { return (kv0 + (size_t)(t0 + r) * a.Hkv) * D; };
+            u32x4 kr[4], vr[4];
+            load4(a.k, kq, dc, t1 - 1 - t0, off, kr);
+            load4(a.v, kq, dc, t1 - 1 - t0, off, vr);
+            store_rows4<KSTR>(k_s, kq, dc, kr);
+            store_transposed4<VSTR>(vt_s, kq, dc, vr);
+        }
+        __syncthreads();
+
+        f32x4 s[2][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ka = as_bf16x8(
+                    *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
+                s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[0][ks], s[0][kb], 0, 0, 0);
+                s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[1][ks], s[1][kb], 0, 0, 0);
+            }
+        }
+        float ml[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = t0 + kb * 16 + 4 * lg + i;
+                    const float x = s[rb][kb][i] * sc;
+                    s[rb][kb][i] = (full || (j < t1 && visible(row_pos[rb], j, P, W))) ? x : -INFINITY;
+                }
+            ml[rb] = s[rb][0][0];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ml[rb] = fmaxf(ml[rb], s[rb][kb][i]);
+        }
+        if (__any(ml[0] > m[0] + kRescaleSlack || ml[1] > m[1] + kRescaleSlack)) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float mt = row_max4(ml[rb]);
+                const bool need = mt > m[rb] + kRescaleSlack;
+                const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
+                m[rb] = need ? mt : m[rb];
+                lp[rb] *= f;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[rb][db] *= f;
+            }
+        }
+        bf16x8 pb[2][PVS];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ps = 0; ps < PVS; ++ps) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i] - m[rb]);
+                    pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i] - m[rb]);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    bf16x2 two = {pb[rb][ps][i], pb[rb][ps][i + 1]};
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, acc, false);
+                }
+            }
+            lp[rb] += acc;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int ps = 0; ps < PVS; ++ps) {
+                const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                    vt_s + (db * 16 + l16) * VSTR + ps * 32 + 8 * lg));
+                o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][ps], o[0][db], 0, 0, 0);
+                o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][ps], o[1][db], 0, 0, 0);
+            }
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float l = row_sum4(lp[rb]);
+        const int r = 32 * wave + 16 * rb + l16;
+        if (row_pos[rb] >= len) continue;
+        const size_t row = ((size_t)b * a.T + row_pos[rb]) * a.Hq + h * G + r % G;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            u32x2 w;
+            w[0] = pack_bf16(o[rb][db][0] * inv, o[rb][db][1] * inv);
+            w[1] = pack_bf16(o[rb][db][2] * inv, o[rb][db][3] * inv);
+            *reinterpret_cast<u32x2*>(a.out + row * D + db * 16 + 4 * lg) = w;
+        }
+        if (lg == 0) a.lse[row] = (m[rb] + __log2f(l)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Di = sum_d dO * O, one thread per (sequence, row, query head).
+template <int D>
+__global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= (size_t)a.B * a.T * a.Hq) return;
+    const int i = (int)((idx / a.Hq) % a.T);
+    const int b = (int)(idx / ((size_t)a.Hq * a.T));
+    if (i >= a.len[b]) return;
+    const u32x4* g = reinterpret_cast<const u32x4*>(a.dout + idx * D);
+    const u32x4* o = reinterpret_cast<const u32x4*>(a.o + idx * D);
+    // A bf16 value is the high half of the float32 with the same bits, so each 32-bit word
+    // holding two bf16 values gives its floats by a shift and a mask.
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const u32x4 x = g[c], y = o[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t xe = x[e], ye = y[e];
+            acc += __uint_as_float(xe << 16) * __uint_as_float(ye << 16);
+            acc += __uint_as_float(xe & 0xffff0000u) * __uint_as_float(ye & 0xffff0000u);
+        }
+    }
+    a.di[idx] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV: one workgroup per (sequence, KV head, 64-key tile). Wave w owns keys
+// k0 + 16 w .. k0 + 16 w + 15. A query step is kBR rows = kBR / G positions x G heads.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int n_ktiles) {
+    constexpr int BP = kBR / G;                 // positions per query step
+    constexpr int KS = D / 32, DB = D / 16, RB = kBR / 16, RS = kBR / 32;
+    constexpr int QSTR = D + 8, TSTR = kBR + 8, CPR = D / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t q_s[kBR * QSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t g_s[kBR * QSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t qt_s[D * TSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t gt_s[D * TSTR];
+    __shared__ __attribute__((aligned(16))) float lse_s[kBR];
+    __shared__ __attribute__((aligned(16))) float di_s[kBR];
+
+    const int total = n_ktiles * a.Hkv * a.B;
+    const int logical = xcd_logical(total);
+    if (logical >= total) return;
+    const int kt = logical % n_ktiles, bh = logical / n_ktiles;
+    const int h = bh % a.Hkv, b = bh / a.Hkv;
+    const int len = a.len[b], P = a.pre[b], W = a.W;
+    const int k0 = kt * kBN;
+    if (k0 >= len) return;
+    const int k1 = min(k0 + kBN, len);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const float sc = a.scale * kLog2e;
+
+    // this lane's key (B-operand column) and its K, V chunks
+    const int key = k0 + 16 * wave + l16;
+    bf16x8 kop[KS], vop[KS];
+    {
+        const size_t off = (((size_t)b * a.T + min(key, k1 - 1)) * a.Hkv + h) * D + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kop[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.k + off + ks * 32));
+            vop[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.v + off + ks * 32));
+        }
+    }
+    f32x4 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // query positions that see some key of the tile
+    const int i_end = k0 < P ? len : min(len, k1 - 1 + W);
+    const int kq = tid % (kBR / 4), dc = tid / (kBR / 4);
+    const size_t row0 = (size_t)b * a.T * a.Hq + h * G;   // (row0 + i * Hq + g) * D
+#pragma unroll 1
+    for (int i0 = k0; i0 < i_end; i0 += BP) {
+        const int i1 = min(i0 + BP, len);             // positions [i0, i1)
+        const int last = (i1 - i0) * G - 1;            // last valid row of the step
+        const bool full = (i1 - i0 == BP) && (k1 - k0 == kBN) && (k1 - 1 <= i0) &&
+                          (k1 - 1 < P || k0 >= (i1 - 1) - W + 1);
+        __syncthreads();
+        if (dc < CPR) {
+            auto off = [&](int r) { return (row0 + (size_t)(i0 + r / G) * a.Hq + r % G) * D; };
+            u32x4 qr[4], gr[4];
+            load4(a.q, kq, dc, last, off, qr);
+            load4(a.dout, kq, dc, last, off, gr);
+            store_rows4<QSTR>(q_s, kq, dc, qr);
+            store_rows4<QSTR>(g_s, kq, dc, gr);
+            store_transposed4<TSTR>(qt_s, kq, dc, qr);
+            store_transposed4<TSTR>(gt_s, kq, dc, gr);
+        }
+        if (tid < kBR) {
+            const int r = min(tid, last);
+            const size_t ri = row0 + (size_t)(i0 + r / G) * a.Hq + r % G;
+            lse_s[tid] = a.lse[ri] * kLog2e;
+            di_s[tid] = a.di[ri];
+        }
+        __syncthreads();
+
+        // S = Q K^T and dP = dO V^T for this wave's 16 keys; lane: rows 16 rb + 4 lg + i
+        f32x4 s[RB], dp[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int e = (rb * 16 + l16) * QSTR + ks * 32 + 8 * lg;
+                const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(q_s + e));
+                const bf16x8 ga = as_bf16x8(*reinterpret_cast<const u32x4*>(g_s + e));
+                s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[ks], s[rb], 0, 0, 0);
+                dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vop[ks], dp[rb], 0, 0, 0);
+            }
+        }
+        // P and dS as A operands of the row contraction (k = rows, order of vt_col)
+        bf16x8 pa[RS], sa[RS];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float4 ls = *reinterpret_cast<const float4*>(lse_s + rb * 16 + 4 * lg);
+            const float4 ds = *reinterpret_cast<const float4*>(di_s + rb * 16 + 4 * lg);
+            const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rb * 16 + 4 * lg + i;
+                const bool vis = full || (r <= last && key < k1 &&
+                                          visible(i0 + r / G, key, P, W));
+                const float p = vis ? __builtin_amdgcn_exp2f(s[rb][i] * sc - lsv[i]) : 0.f;
+                const float d = p * (dp[rb][i] - dsv[i]);
+                pa[rb / 2][(rb & 1) * 4 + i] = (__bf16)p;
+                sa[rb / 2][(rb & 1) * 4 + i] = (__bf16)d;
+            }
+        }
+        // dV += P^T dO, dK += dS^T Q (scaled at the end)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int rs = 0; rs < RS; ++rs) {
+                const int e = (db * 16 + l16) * TSTR + rs * 32 + 8 * lg;
+                const bf16x8 gb = as_bf16x8(*reinterpret_cast<const u32x4*>(gt_s + e));
+                const bf16x8 qb = as_bf16x8(*reinterpret_cast<const u32x4*>(qt_s + e));
+                dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rs], gb, dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[rs], qb, dk[db], 0, 0, 0);
+            }
+    }
+
+    // lane holds keys 16 w + 4 lg + i, dims 16 db + l16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = k0 + 16 * wave + 4 * lg + i;
+        if (j >= k1) continue;
+        const size_t row = (((size_t)b * a.T + j) * a.Hkv + h) * D + l16;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            a.dk[row + db * 16] = __builtin_bit_cast(uint16_t, (__bf16)(dk[db][i] * a.scale));
+            a.dv[row + db * 16] = __builtin_bit_cast(uint16_t, (__bf16)dv[db][i]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ: one workgroup per (sequence, KV head, 128-row query tile), walking its key tiles.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_qtiles) {
+    constexpr int BQ = kRows / G;
+    constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
+    constexpr int KSTR = D + 8, TSTR = kBN + 8, CPR = D / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t kt_s[D * TSTR];
+
+    const int total = n_qtiles * a.Hkv * a.B;
+    const int logical = xcd_logical(total);
+    if (logical >= total) return;
+    const int qt = logical % n_qtiles, bh = logical / n_qtiles;
+    const int h = bh % a.Hkv, b = bh / a.Hkv;
+    const int len = a.len[b], P = a.pre[b], W = a.W;
+    const int c0 = qt * BQ;
+    if (c0 >= len) return;
+    const int p_lo = c0, p_hi = min(c0 + BQ, len) - 1;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const float sc = a.scale * kLog2e;
+
+    int row_pos[2];
+    size_t row_idx[2];
+    bf16x8 qop[2][KS], gop[2][KS];
+    float lse2[2], di[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = 32 * wave + 16 * rb + l16;
+        row_pos[rb] = c0 + r / G;
+        const int cl = min(row_pos[rb], len - 1);
+        row_idx[rb] = ((size_t)b * a.T + cl) * a.Hq + h * G + r % G;
+        const size_t off = row_idx[rb] * D + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.q + off + ks * 32));
+            gop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.dout + off + ks * 32));
+        }
+        lse2[rb] = a.lse[row_idx[rb]] * kLog2e;
+        di[rb] = a.di[row_idx[rb]];
+    }
+    f32x4 acc[2][DB];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const KeyWalk wk{min(P, p_hi + 1), max(P, p_lo - W + 1), p_hi + 1};
+    const size_t kv0 = (size_t)b * a.T * a.Hkv + h;
+    const int kq = tid % (kBN / 4), dc = tid / (kBN / 4);
+    int seg = 0, t0 = -kBN;
+#pragma unroll 1
+    while (wk.next(seg, t0)) {
+        const int t1 = min(t0 + kBN, seg == 0 ? wk.hi0 : wk.hi1);
+        const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) && (t1 - 1 < P || t0 >= p_hi - W + 1);
+        __syncthreads();
+        if (dc < CPR) {
+            auto off = [&](int r) { return (kv0 + (size_t)(t0 + r) * a.Hkv) * D; };
+            u32x4 kr[4], vr[4];
+            load4(a.k, kq, dc, t1 - 1 - t0, off, kr);
+            load4(a.v, kq, dc, t1 - 1 - t0, off, vr);
+            store_rows4<KSTR>(k_s, kq, dc, kr);
+            store_rows4<KSTR>(v_s, kq, dc, vr);
+            store_transposed4<TSTR>(kt_s, kq, dc, kr);
+        }
+        __syncthreads();
+
+        // S^T = K Q^T, dP^T = V dO^T; lane: keys 16 kb + 4 lg + i, row l16
+        f32x4 s[2][KB], dp[2][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dp[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int e = (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg;
+                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(k_s + e));
+                const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(v_s + e));
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[rb][ks], s[rb][kb], 0, 0, 0);
+                    dp[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gop[rb][ks], dp[rb][kb], 0, 0, 0);
+                }
+            }
+        }
+        // dS^T as B operands (k = keys in vt_col order)
+        bf16x8 sb[2][PVS];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = t0 + kb * 16 + 4 * lg + i;
+                    const bool vis = full || (j < t1 && visible(row_pos[rb], j, P, W));
+                    const float p = vis ? __builtin_amdgcn_exp2f(s[rb][kb][i] * sc - lse2[rb]) : 0.f;
+                    sb[rb][kb / 2][(kb & 1) * 4 + i] = (__bf16)(p * (dp[rb][kb][i] - di[rb]));
+                }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int ps = 0; ps < PVS; ++ps) {
+                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                    kt_s + (db * 16 + l16) * TSTR + ps * 32 + 8 * lg));
+                acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[0][ps], acc[0][db], 0, 0, 0);
+                acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[1][ps], acc[1][db], 0, 0, 0);
+            }
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        if (row_pos[rb] >= len) continue;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            u32x2 w;
+            w[0] = pack_bf16(acc[rb][db][0] * a.scale, acc[rb][db][1] * a.scale);
+            w[1] = pack_bf16(acc[rb][db][2] * a.scale, acc[rb][db][3] * a.scale);
+            *reinterpret_cast<u32x2*>(a.dq + row_idx[rb] * D + db * 16 + 4 * lg) = w;
+        }
+    }
+}
+
+template <int D, int G>
+hipError_t launch_train_g(const TrainArgs& a, bool backward, hipStream_t s) {
+    constexpr int BQ = kRows / G;
+    const int n_qtiles = (a.T + BQ - 1) / BQ;
+    const int q_total = n_qtiles * a.Hkv * a.B;
+    const int q_grid = ((q_total + 7) / 8) * 8;
+    if (!backward) {
+        hipLaunchKernelGGL((train_fwd_kernel<D, G>), dim3(q_grid), dim3(kBlock), 0, s, a, n_qtiles);
+        return hipGetLastError();
+    }
+    const size_t rows = (size_t)a.B * a.T * a.Hq;
+    hipLaunchKernelGGL((train_rowdot_kernel<D>), dim3((unsigned)((rows + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_ktiles = (a.T + kBN - 1) / kBN;
+    const int k_total = n_ktiles * a.Hkv * a.B;
+    hipLaunchKernelGGL((train_dkdv_kernel<D, G>), dim3(((k_total + 7) / 8) * 8), dim3(kBlock), 0, s,
+                       a, n_ktiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((train_dq_kernel<D, G>), dim3(q_grid), dim3(kBlock), 0, s, a, n_qtiles);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_train_d(const TrainArgs& a, int G, bool backward, hipStream_t s) {
+    switch (G) {
+        case 1: return launch_train_g<D, 1>(a, backward, s);
+        case 2: return launch_train_g<D, 2>(a, backward, s);
+        case 4: return launch_train_g<D, 4>(a, backward, s);
+        default: return launch_train_g<D, 8>(a, backward, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_train(const TrainLaunch& t, hipStream_t s) {
+    TrainArgs a;
+    a.q = (const uint16_t*)t.q;
+    a.k = (const uint16_t*)t.k;
+    a.v = (const uint16_t*)t.v;
+    a.o = (const uint16_t*)t.out;
+    a.dout = (const uint16_t*)t.dout;
+    a.out = (uint16_t*)t.out;
+    a.dq = (uint16_t*)t.dq;
+    a.dk = (uint16_t*)t.dk;
+    a.dv = (uint16_t*)t.dv;
+    a.lse = t.lse;
+    a.di = t.di;
+    a.pre = t.pre;
+    a.len = t.len;
+    a.B = t.B;
+    a.T = t.T;
+    a.Hq = t.Hq;
+    a.Hkv = t.Hkv;
+    a.W = t.W;
+    a.scale = t.scale;
+    const int G = t.Hq / t.Hkv;
+    return t.D == 128 ? launch_train_d<128>(a, G, t.backward, s)
+                      : launch_train_d<64>(a, G, t.backward, s);
+}
+
+}  // namespace psa

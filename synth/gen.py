@@ -33,6 +33,7 @@ import torch
 STREAM_Q = 1
 STREAM_K = 2
 STREAM_V = 3
+STREAM_DO = 4   # output gradients of the training workloads
 
 _M64 = 1 << 64
 

@@ -98,3 +98,19 @@ def test_gradient_identities():
     np.testing.assert_allclose(dq1, 0.0, atol=1e-12)      # softmax over one key is constant
     np.testing.assert_allclose(dk1, 0.0, atol=1e-12)
     np.testing.assert_allclose(dv1, g.reshape(T, Hkv, G, D).sum(axis=2), atol=1e-12)
+
+
+def test_row_restricted_forms_equal_the_full_ones():
+    rng = np.random.default_rng(13)
+    T, P, W, Hq, Hkv, D = 37, 6, 9, 4, 2, 8
+    q, k, v, g = rnd(rng, T, Hq, D), rnd(rng, T, Hkv, D), rnd(rng, T, Hkv, D), rnd(rng, T, Hq, D)
+    out, lse = train.forward(q, k, v, P, W, 0.3)
+    dq, dk, dv = train.backward(q, k, v, g, P, W, 0.3)
+    rows = [0, 3, 5, 6, 7, 20, 36]
+    o2, l2 = train.forward_rows(q, k, v, P, W, 0.3, rows)
+    np.testing.assert_allclose(o2, out[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, lse[rows], rtol=0, atol=1e-12)
+    dq2, dk2, dv2 = train.backward_rows(q, k, v, g, P, W, 0.3, rows, rows)
+    np.testing.assert_allclose(dq2, dq[rows], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk2, dk[rows], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv2, dv[rows], rtol=0, atol=1e-11)
