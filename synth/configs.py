@@ -47,9 +47,6 @@ class Workload:
     def window_of(self, b: int) -> int:
         return self.window if self.windows is None else self.windows[b]
 
-    def visible_tokens(self, n: List[int]) -> int:
-        """Sum over sequences of the visible count min(n_b, P_b + w_b) for history lengths n."""
-        return sum(min(nb, pb + self.window_of(b)) for b, (nb, pb) in enumerate(zip(n, self.prefix)))
 
 
 def tiny_fp32(seed: int = 0) -> Workload:

@@ -57,4 +57,5 @@ def test_workload_draws_are_seeded_and_in_range():
     assert all(1000 <= t <= 131072 for t in w.start)
     pre = configs.prefill_chunk512()
     assert all(8192 <= t <= 65536 for t in pre.start)
-    assert configs.decode_p100_w4096().visible_tokens([32768] * 64) == 64 * 4196
+    d = configs.decode_p100_w4096()
+    assert (d.batch, d.window, d.prefix[0], d.start[0]) == (64, 4096, 100, 32768)
