@@ -222,6 +222,113 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int ti
     if (dc < CPR) store_transposed4<VSTR>(vt_s, kq, dc, vreg);
 }
 
+// Online-softmax state of one lane's two row blocks. m: running maximum (log2 domain),
+// kNeg until a row has seen a visible key; mb: the value the S accumulator starts from
+// (m once set, else 0), so the products arrive already shifted and exp2 needs no
+// subtraction; o: O^T accumulators; l: row sums, accumulated by an MFMA against an all-ones
+// A operand (every element of l[rb] holds the row's sum of the bf16-rounded probabilities,
+// the same values that weight V).
+template <int DB>
+struct SoftmaxRows {
+    f32x4 o[2][DB];
+    f32x4 l[2];
+    float m[2], mb[2];
+};
+
+// One 64-key tile for a wave's 32 rows: S^T = K Q^T - mb, the mask (edge tiles only), the
+// running-max update, P^T = exp2(S^T) as bf16 B operands, then O^T += V^T P^T and
+// l += 1 P^T.
+template <int D>
+__device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
+                                          const uint16_t* k_s, const uint16_t* vt_s,
+                                          const int (&row_pos)[2], int ct0, int t1, int P, int W,
+                                          int l16, int lg, bool masked) {
+    constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
+    constexpr int KSTR = D + 8, VSTR = kBN + 8;
+    f32x4 s[2][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        s[0][kb] = f32x4{-st.mb[0], -st.mb[0], -st.mb[0], -st.mb[0]};
+        s[1][kb] = f32x4{-st.mb[1], -st.mb[1], -st.mb[1], -st.mb[1]};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1][ks], s[1][kb], 0, 0, 0);
+        }
+    }
+    // Masked logits become -inf: exp2(-inf) is 0 for any finite shift.
+    float ml[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        if (masked) {
+            const int p = row_pos[rb];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = ct0 + kb * 16 + 4 * lg + i;
+                    const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
+                    s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
+                }
+        }
+        ml[rb] = fmaxf(s[rb][0][0], s[rb][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = (kb == 0 ? 2 : 0); i < 4; i += 2)
+                ml[rb] = __builtin_fmaxf(__builtin_fmaxf(ml[rb], s[rb][kb][i]), s[rb][kb][i + 1]);
+    }
+    // The running max of a row only moves when some lane's own max exceeds it by the slack
+    // (or the row has none yet); test that with one ballot, do the cross-lane max only then.
+    if (__any(ml[0] + st.mb[0] > st.m[0] + kRescaleSlack ||
+              ml[1] + st.mb[1] > st.m[1] + kRescaleSlack)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float mt = row_max4(ml[rb]) + st.mb[rb];   // absolute tile max
+            const bool need = mt > st.m[rb] + kRescaleSlack;
+            if (need) {
+                const float f = __builtin_amdgcn_exp2f(st.m[rb] - mt);
+                const float shift = mt - st.mb[rb];
+                st.m[rb] = mt;
+                st.mb[rb] = mt;
+                st.l[rb] *= f;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) st.o[rb][db] *= f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[rb][kb] -= shift;
+            }
+        }
+    }
+    bf16x8 pb[2][PVS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ps = 0; ps < PVS; ++ps)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i]);
+                pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i]);
+            }
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int ps = 0; ps < PVS; ++ps) {
+        st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][ps], st.l[0], 0, 0, 0);
+        st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][ps], st.l[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int ps = 0; ps < PVS; ++ps) {
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                vt_s + (db * 16 + l16) * VSTR + ps * 32 + 8 * lg));
+            st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], st.o[0][db], 0, 0, 0);
+            st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], st.o[1][db], 0, 0, 0);
+        }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
                                                             uint16_t* __restrict__ out,
@@ -284,14 +391,14 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
             qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage_q + q_off[rb] + ks * 32));
     }
 
-    f32x4 o[2][DB];
-    float m[2], lp[2];
+    SoftmaxRows<DB> st;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        m[rb] = kNeg;
-        lp[rb] = 0.f;
+        st.m[rb] = kNeg;
+        st.mb[rb] = 0.f;
+        st.l[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) st.o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const size_t head_off = ((size_t)b * c.Hkv + h) * (size_t)c.S * D;
@@ -340,96 +447,13 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
             fetch_tile<D, kBN, kBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
         __syncthreads();
 
-        // ---- S^T = K Q^T ----------------------------------------------------------------
-        f32x4 s[2][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
-                s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0][ks], s[0][kb], 0, 0, 0);
-                s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1][ks], s[1][kb], 0, 0, 0);
-            }
-        }
-
-        // ---- mask, online softmax -------------------------------------------------------
-        // Masked logits become -inf: exp2(-inf - m) is 0 for the finite running max m, which
-        // starts at kNeg and is only ever raised to a real tile maximum.
-        bf16x8 pb[2][PVS];
-        float ml[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            if (!full) {
-                const int p = row_pos[rb];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = ct0 + kb * 16 + 4 * lg + i;
-                        const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
-                        s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
-                    }
-            }
-            ml[rb] = fmaxf(s[rb][0][0], s[rb][0][1]);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = (kb == 0 ? 2 : 0); i < 4; i += 2)
-                    ml[rb] = __builtin_fmaxf(__builtin_fmaxf(ml[rb], s[rb][kb][i]), s[rb][kb][i + 1]);
-        }
-        // The running max of a row only moves when some lane's own max exceeds it by the
-        // slack; test that with one ballot and do the cross-lane row max only then.
-        if (__any(ml[0] > m[0] + kRescaleSlack || ml[1] > m[1] + kRescaleSlack)) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const float mt = row_max4(ml[rb]);
-                const bool need = mt > m[rb] + kRescaleSlack;
-                const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
-                m[rb] = need ? mt : m[rb];
-                lp[rb] *= f;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) o[rb][db] *= f;
-            }
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            // probabilities -> bf16 B operands; their row sum from the same rounded values
-            float acc = 0.f;
-#pragma unroll
-            for (int ps = 0; ps < PVS; ++ps) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i] - m[rb]);
-                    pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i] - m[rb]);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    bf16x2 two = {pb[rb][ps][i], pb[rb][ps][i + 1]};
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, acc, false);
-                }
-            }
-            lp[rb] += acc;
-        }
-
-        // ---- O^T += V^T P^T -------------------------------------------------------------
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int ps = 0; ps < PVS; ++ps) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                    vt_s + (db * 16 + l16) * VSTR + ps * 32 + 8 * lg));
-                o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], o[0][db], 0, 0, 0);
-                o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], o[1][db], 0, 0, 0);
-            }
+        tile_step<D>(st, qop, k_s, vt_s, row_pos, ct0, t1, P, W, l16, lg, !full);
     }
 
     // ---- normalise and write -------------------------------------------------------------
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const float l = row_sum4(lp[rb]);
+        const float l = st.l[rb][0];
         const int r = 32 * wave + 16 * rb + l16;
         const int cl = c0 + r / G;
         if (cl >= chunk) continue;
@@ -439,14 +463,14 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             u32x2 w;
-            const __bf16 e0 = (__bf16)(o[rb][db][0] * inv), e1 = (__bf16)(o[rb][db][1] * inv);
-            const __bf16 e2 = (__bf16)(o[rb][db][2] * inv), e3 = (__bf16)(o[rb][db][3] * inv);
+            const __bf16 e0 = (__bf16)(st.o[rb][db][0] * inv), e1 = (__bf16)(st.o[rb][db][1] * inv);
+            const __bf16 e2 = (__bf16)(st.o[rb][db][2] * inv), e3 = (__bf16)(st.o[rb][db][3] * inv);
             w[0] = (uint32_t)__builtin_bit_cast(uint16_t, e0) | ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
             w[1] = (uint32_t)__builtin_bit_cast(uint16_t, e2) | ((uint32_t)__builtin_bit_cast(uint16_t, e3) << 16);
             *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * lg) = w;
         }
         if (lse != nullptr && lg == 0)
-            lse[((size_t)b * chunk + cl) * c.Hq + hq] = (m[rb] + __log2f(l)) * kLn2;
+            lse[((size_t)b * chunk + cl) * c.Hq + hq] = (st.m[rb] + __log2f(l)) * kLn2;
     }
 }
 
