@@ -117,3 +117,33 @@ def test_status_strings(psa):
     for s in range(5):
         assert psa.lib.psa_status_string(s).decode()
     assert psa.lib.psa_status_string(99).decode() == "unknown status"
+
+
+def test_train_workspace_and_validation(psa):
+    lib = psa.lib
+    d = psa.TrainDesc(4, 1000, 16, 8, 128, 256, 0.0, 0)
+    n = lib.psa_train_workspace_bytes(ctypes.byref(d))
+    assert n >= 4 * 1000 * 16 * 4 and n % 256 == 0       # float32 Di per (row, head)
+    for bad in [psa.TrainDesc(0, 1000, 16, 8, 128, 256, 0.0, 0),
+                psa.TrainDesc(4, 0, 16, 8, 128, 256, 0.0, 0),
+                psa.TrainDesc(4, 1000, 12, 8, 128, 256, 0.0, 0),
+                psa.TrainDesc(4, 1000, 48, 3, 128, 256, 0.0, 0),
+                psa.TrainDesc(4, 1000, 16, 8, 96, 256, 0.0, 0),
+                psa.TrainDesc(4, 1000, 16, 8, 128, 0, 0.0, 0),
+                psa.TrainDesc(4, 1000, 16, 8, 128, 256, -1.0, 0),
+                psa.TrainDesc(4, 1000, 16, 8, 128, 256, 0.0, 7)]:
+        assert lib.psa_train_workspace_bytes(ctypes.byref(bad)) == 0
+        assert lib.psa_last_error()
+    # null pointers are rejected on the host (nothing reaches the device)
+    pre = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    rc = lib.psa_train_fwd(ctypes.byref(d), pre, None, None, None, None, None, None, None, 0, None)
+    assert rc == psa.PSA_ERR_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
