@@ -31,7 +31,7 @@ def tol_check(out: np.ndarray, ref: np.ndarray, dtype, what=""):
 
 
 def oracle_decode(wl, b, p, q_row):
-    return attn.decode_query(q_row, p, drive.hist_provider(wl, b), wl.prefix[b], wl.window,
+    return attn.decode_query(q_row, p, drive.hist_provider(wl, b), wl.prefix[b], wl.window_of(b),
                              wl.n_kv_heads, wl.rope_base, wl.scale)
 
 
@@ -144,6 +144,13 @@ def test_decode_p100_w4096_full_size():
 
 def test_decode_p512_w16384_full_size():
     run_full(configs.decode_p512_w16384(), [0, 13, 31])
+
+
+def test_decode_ragged_window_full_size():
+    # a window length per sequence (set after reset): the shortest, a middle and the longest
+    wl = configs.decode_ragged_window()
+    order = sorted(range(wl.batch), key=lambda b: wl.windows[b])
+    run_full(wl, [order[0], order[1], order[wl.batch // 2], order[-1]])
 
 
 def test_ragged_decode_64_steps():
