@@ -70,6 +70,23 @@ __device__ __forceinline__ void store_transposed4(uint16_t* vt_s, int kq, int dc
     }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed MFMA operand from a row-major bf16 tile in LDS (ds_read_b64_tr_b16, gfx950).
+// Within each 16-lane group the instruction takes the 16 lanes' 4-element reads as a 16 x 4
+// tile T and hands lane i the elements T[i / 4 + 4 j][i % 4], j = 0..3. So if lane k of a
+// group reads row r0 + k / 4 at column c0 + 4 (k % 4), lane i receives column c0 + i of
+// rows r0 .. r0 + 3. Two reads (rows r0 .. r0 + 3 and r1 .. r1 + 3) fill the 8 k-values of
+// one operand. `p0`, `p1`: this lane's addresses for the two reads (8-byte aligned).
+__device__ __forceinline__ bf16x8 lds_read_tr2(const uint16_t* p0, const uint16_t* p1) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
 // Two bf16 values packed into one 32-bit word (first in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |

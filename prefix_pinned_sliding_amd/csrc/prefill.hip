@@ -193,22 +193,15 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
         const int kk = ci / CPR, col = ci % CPR;
         const uint32_t e = __umul24((uint32_t)row(min(kk, last)), (uint32_t)stride) + col * 8;
         kreg[rr] = *reinterpret_cast<const u32x4*>(kb + e);
-    }
-    const int kq = tid % (BN / 4), dc = tid / (BN / 4);
-    if (dc < CPR) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t e = __umul24((uint32_t)row(min(4 * kq + q, last)), (uint32_t)stride) + dc * 8;
-            vreg[q] = *reinterpret_cast<const u32x4*>(vb + e);
-        }
+        vreg[rr] = *reinterpret_cast<const u32x4*>(vb + e);
     }
 }
 
 
-// Registers -> LDS: K rows as they are, V transposed (4 keys x 8 dims -> 8 rows of V^T
-// holding 4 keys each, columns permuted by vt_col).
-template <int D, int BN, int NT, int KSTR, int VSTR>
-__device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int tid,
+// Registers -> LDS: K and V rows as they are (consecutive lanes on consecutive 16-byte
+// chunks of a row); V^T operands are read back with transposing LDS loads.
+template <int D, int BN, int NT, int KSTR>
+__device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* v_s, int tid,
                                            const u32x4* kreg, const u32x4* vreg) {
     constexpr int CPR = D / 8;
     constexpr int KLD = (BN * CPR) / NT;
@@ -217,9 +210,8 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* vt_s, int ti
         const int ci = tid + NT * rr;
         const int kk = ci / CPR, col = ci % CPR;
         *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
+        *reinterpret_cast<u32x4*>(v_s + kk * KSTR + col * 8) = vreg[rr];
     }
-    const int kq = tid % (BN / 4), dc = tid / (BN / 4);
-    if (dc < CPR) store_transposed4<VSTR>(vt_s, kq, dc, vreg);
 }
 
 // Online-softmax state of one lane's two row blocks. m: running maximum (log2 domain),
@@ -240,11 +232,11 @@ struct SoftmaxRows {
 // l += 1 P^T.
 template <int D>
 __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
-                                          const uint16_t* k_s, const uint16_t* vt_s,
+                                          const uint16_t* k_s, const uint16_t* v_s,
                                           const int (&row_pos)[2], int ct0, int t1, int P, int W,
                                           int l16, int lg, bool masked) {
     constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    constexpr int KSTR = D + 8, VSTR = kBN + 8;
+    constexpr int KSTR = D + 8;
     f32x4 s[2][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -318,12 +310,14 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
         st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][ps], st.l[0], 0, 0, 0);
         st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][ps], st.l[1], 0, 0, 0);
     }
+    // V^T operand (d = 16 db + l16; keys in the order of P^T's accumulator layout:
+    // 32 ps + 4 lg + j, then 32 ps + 16 + 4 lg + j) by two transposing reads of V rows
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int ps = 0; ps < PVS; ++ps) {
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                vt_s + (db * 16 + l16) * VSTR + ps * 32 + 8 * lg));
+            const uint16_t* v0 = v_s + (32 * ps + 4 * lg + l16 / 4) * KSTR + db * 16 + 4 * (l16 % 4);
+            const bf16x8 a = lds_read_tr2(v0, v0 + 16 * KSTR);
             st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], st.o[0][db], 0, 0, 0);
             st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], st.o[1][db], 0, 0, 0);
         }
@@ -341,12 +335,11 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
     constexpr int KB = kBN / 16;          // key blocks per tile
     constexpr int PVS = kBN / 32;         // k-steps of O^T = V^T P^T
     constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
-    constexpr int VSTR = kBN + 8;         // LDS row stride of V^T (elements; 36 dwords)
     constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int KLD = (kBN * CPR) / kBlock;
 
     __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
 
     // XCD-aware tile order: workgroup L runs on XCD L % 8; give each XCD a contiguous run
     // of logical tiles so all query tiles of one (sequence, KV head) share that XCD's L2.
@@ -419,7 +412,7 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
                       (const uint16_t*)(pid >= 0 ? c.pool_v : c.v) + pre_off,
                       (size_t)b * chunk, n, c.pre[b], c.W, c.Pmax, c.Hkv, h};
 
-    u32x4 kreg[KLD], vreg[4];
+    u32x4 kreg[KLD], vreg[KLD];
     int seg = 0, t0 = -kBN;
     bool have = walk_next<kBN>(wk, seg, t0);
     if (PSA_PREFILL_PIPELINE && have)
@@ -441,13 +434,13 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
                           (t1 - 1 < P || ct0 >= p_hi - W + 1);
         __syncthreads();                  // the previous tile's LDS reads are done
         if (!PSA_PREFILL_PIPELINE) fetch_tile<D, kBN, kBlock>(src, cseg, ct0, t1, tid, kreg, vreg);
-        stage_tile<D, kBN, kBlock, KSTR, VSTR>(k_s, vt_s, tid, kreg, vreg);
+        stage_tile<D, kBN, kBlock, KSTR>(k_s, v_s, tid, kreg, vreg);
         have = walk_next<kBN>(wk, seg, t0);
         if (PSA_PREFILL_PIPELINE && have)   // in flight while this tile is computed
             fetch_tile<D, kBN, kBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
         __syncthreads();
 
-        tile_step<D>(st, qop, k_s, vt_s, row_pos, ct0, t1, P, W, l16, lg, !full);
+        tile_step<D>(st, qop, k_s, v_s, row_pos, ct0, t1, P, W, l16, lg, !full);
     }
 
     // ---- normalise and write -------------------------------------------------------------
