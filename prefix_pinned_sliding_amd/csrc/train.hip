@@ -66,21 +66,40 @@ struct KeyWalk {
     }
 };
 
-// Row-major copy of 4 rows x 16 bytes per thread: rows 4kq .. 4kq + 3, chunk dc, with row
-// r at src + off(r) (off: element offset), rows beyond `last` reading row `last`.
-template <typename Off>
-__device__ __forceinline__ void load4(const uint16_t* src, int kq, int dc, int last, Off off,
-                                      u32x4* r) {
+// Row-major copy of a ROWS x D tile through registers: consecutive lanes take consecutive
+// 16-byte chunks of a row (conflict-free LDS stores); row r comes from src + off(r) (element
+// offset), rows beyond `last` repeat row `last`. Transposed operands are read back from the
+// row-major copy with ds_read_b64_tr_b16 (lds_read_tr2).
+template <int D, int ROWS>
+struct RowTile {
+    static constexpr int CPR = D / 8;
+    static constexpr int N = ROWS * CPR / kBlock;
+    u32x4 r[N];
+    template <typename Off>
+    __device__ __forceinline__ void load(const uint16_t* src, int tid, int last, Off off) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-        r[x] = *reinterpret_cast<const u32x4*>(src + off(min(4 * kq + x, last)) + dc * 8);
-}
+        for (int x = 0; x < N; ++x) {
+            const int ci = tid + kBlock * x;
+            r[x] = *reinterpret_cast<const u32x4*>(src + off(min(ci / CPR, last)) + (ci % CPR) * 8);
+        }
+    }
+    template <int STR>
+    __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+        for (int x = 0; x < N; ++x) {
+            const int ci = tid + kBlock * x;
+            *reinterpret_cast<u32x4*>(dst + (ci / CPR) * STR + (ci % CPR) * 8) = r[x];
+        }
+    }
+};
 
+// The transposed operand for rows 32 s + 4 lg + j (slots 0..3) and 32 s + 16 + 4 lg + j
+// (slots 4..7), column c0 + l16, of a row-major tile with row stride STR: the k order of
+// an accumulator pair (rows 0..15 and 16..31 of a 32-row group).
 template <int STR>
-__device__ __forceinline__ void store_rows4(uint16_t* dst, int kq, int dc, const u32x4* r) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-        *reinterpret_cast<u32x4*>(dst + (4 * kq + x) * STR + dc * 8) = r[x];
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int s32, int c0, int l16, int lg) {
+    const uint16_t* p = tile + (32 * s32 + 4 * lg + l16 / 4) * STR + c0 + 4 * (l16 % 4);
+    return lds_read_tr2(p, p + 16 * STR);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -89,9 +108,9 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n_qtiles) {
     constexpr int BQ = kRows / G;
     constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    constexpr int KSTR = D + 8, VSTR = kBN + 8, CPR = D / 8;
+    constexpr int KSTR = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
 
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
@@ -128,20 +147,19 @@ __global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n
 
     const KeyWalk wk{min(P, p_hi + 1), max(P, p_lo - W + 1), p_hi + 1};
     const size_t kv0 = (size_t)b * a.T * a.Hkv + h;   // row j at (kv0 + j * Hkv) * D
-    const int kq = tid % (kBN / 4), dc = tid / (kBN / 4);
     int seg = 0, t0 = -kBN;
 #pragma unroll 1
     while (wk.next(seg, t0)) {
         const int t1 = min(t0 + kBN, seg == 0 ? wk.hi0 : wk.hi1);
         const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) && (t1 - 1 < P || t0 >= p_hi - W + 1);
         __syncthreads();
-        if (dc < CPR) {
+        {
             auto off = [&](int r) { return (kv0 + (size_t)(t0 + r) * a.Hkv) * D; };
-            u32x4 kr[4], vr[4];
-            load4(a.k, kq, dc, t1 - 1 - t0, off, kr);
-            load4(a.v, kq, dc, t1 - 1 - t0, off, vr);
-            store_rows4<KSTR>(k_s, kq, dc, kr);
-            store_transposed4<VSTR>(vt_s, kq, dc, vr);
+            RowTile<D, kBN> kr, vr;
+            kr.load(a.k, tid, t1 - 1 - t0, off);
+            vr.load(a.v, tid, t1 - 1 - t0, off);
+            kr.template store<KSTR>(k_s, tid);
+            vr.template store<KSTR>(v_s, tid);
         }
         __syncthreads();
 
@@ -210,8 +228,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int ps = 0; ps < PVS; ++ps) {
-                const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                    vt_s + (db * 16 + l16) * VSTR + ps * 32 + 8 * lg));
+                const bf16x8 va = tr_operand<KSTR>(v_s, ps, db * 16, l16, lg);
                 o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][ps], o[0][db], 0, 0, 0);
                 o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][ps], o[1][db], 0, 0, 0);
             }
@@ -269,11 +286,9 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int n_ktiles) {
     constexpr int BP = kBR / G;                 // positions per query step
     constexpr int KS = D / 32, DB = D / 16, RB = kBR / 16, RS = kBR / 32;
-    constexpr int QSTR = D + 8, TSTR = kBR + 8, CPR = D / 8;
+    constexpr int QSTR = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t q_s[kBR * QSTR];
     __shared__ __attribute__((aligned(16))) uint16_t g_s[kBR * QSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t qt_s[D * TSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t gt_s[D * TSTR];
     __shared__ __attribute__((aligned(16))) float lse_s[kBR];
     __shared__ __attribute__((aligned(16))) float di_s[kBR];
 
@@ -311,7 +326,6 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
 
     // query positions that see some key of the tile
     const int i_end = k0 < P ? len : min(len, k1 - 1 + W);
-    const int kq = tid % (kBR / 4), dc = tid / (kBR / 4);
     const size_t row0 = (size_t)b * a.T * a.Hq + h * G;   // (row0 + i * Hq + g) * D
 #pragma unroll 1
     for (int i0 = k0; i0 < i_end; i0 += BP) {
@@ -320,15 +334,13 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         const bool full = (i1 - i0 == BP) && (k1 - k0 == kBN) && (k1 - 1 <= i0) &&
                           (k1 - 1 < P || k0 >= (i1 - 1) - W + 1);
         __syncthreads();
-        if (dc < CPR) {
+        {
             auto off = [&](int r) { return (row0 + (size_t)(i0 + r / G) * a.Hq + r % G) * D; };
-            u32x4 qr[4], gr[4];
-            load4(a.q, kq, dc, last, off, qr);
-            load4(a.dout, kq, dc, last, off, gr);
-            store_rows4<QSTR>(q_s, kq, dc, qr);
-            store_rows4<QSTR>(g_s, kq, dc, gr);
-            store_transposed4<TSTR>(qt_s, kq, dc, qr);
-            store_transposed4<TSTR>(gt_s, kq, dc, gr);
+            RowTile<D, kBR> qr, gr;
+            qr.load(a.q, tid, last, off);
+            gr.load(a.dout, tid, last, off);
+            qr.template store<QSTR>(q_s, tid);
+            gr.template store<QSTR>(g_s, tid);
         }
         if (tid < kBR) {
             const int r = min(tid, last);
@@ -376,9 +388,8 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int rs = 0; rs < RS; ++rs) {
-                const int e = (db * 16 + l16) * TSTR + rs * 32 + 8 * lg;
-                const bf16x8 gb = as_bf16x8(*reinterpret_cast<const u32x4*>(gt_s + e));
-                const bf16x8 qb = as_bf16x8(*reinterpret_cast<const u32x4*>(qt_s + e));
+                const bf16x8 gb = tr_operand<QSTR>(g_s, rs, db * 16, l16, lg);
+                const bf16x8 qb = tr_operand<QSTR>(q_s, rs, db * 16, l16, lg);
                 dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rs], gb, dv[db], 0, 0, 0);
                 dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[rs], qb, dk[db], 0, 0, 0);
             }
@@ -404,10 +415,9 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_qtiles) {
     constexpr int BQ = kRows / G;
     constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    constexpr int KSTR = D + 8, TSTR = kBN + 8, CPR = D / 8;
+    constexpr int KSTR = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t kt_s[D * TSTR];
 
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
@@ -450,21 +460,19 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
 
     const KeyWalk wk{min(P, p_hi + 1), max(P, p_lo - W + 1), p_hi + 1};
     const size_t kv0 = (size_t)b * a.T * a.Hkv + h;
-    const int kq = tid % (kBN / 4), dc = tid / (kBN / 4);
     int seg = 0, t0 = -kBN;
 #pragma unroll 1
     while (wk.next(seg, t0)) {
         const int t1 = min(t0 + kBN, seg == 0 ? wk.hi0 : wk.hi1);
         const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) && (t1 - 1 < P || t0 >= p_hi - W + 1);
         __syncthreads();
-        if (dc < CPR) {
+        {
             auto off = [&](int r) { return (kv0 + (size_t)(t0 + r) * a.Hkv) * D; };
-            u32x4 kr[4], vr[4];
-            load4(a.k, kq, dc, t1 - 1 - t0, off, kr);
-            load4(a.v, kq, dc, t1 - 1 - t0, off, vr);
-            store_rows4<KSTR>(k_s, kq, dc, kr);
-            store_rows4<KSTR>(v_s, kq, dc, vr);
-            store_transposed4<TSTR>(kt_s, kq, dc, kr);
+            RowTile<D, kBN> kr, vr;
+            kr.load(a.k, tid, t1 - 1 - t0, off);
+            vr.load(a.v, tid, t1 - 1 - t0, off);
+            kr.template store<KSTR>(k_s, tid);
+            vr.template store<KSTR>(v_s, tid);
         }
         __syncthreads();
 
@@ -507,8 +515,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int ps = 0; ps < PVS; ++ps) {
-                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                    kt_s + (db * 16 + l16) * TSTR + ps * 32 + 8 * lg));
+                const bf16x8 ka = tr_operand<KSTR>(k_s, ps, db * 16, l16, lg);
                 acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[0][ps], acc[0][db], 0, 0, 0);
                 acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[1][ps], acc[1][db], 0, 0, 0);
             }
