@@ -147,3 +147,18 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    # the binding has no fallback: a package tree without libpsa.so must not import
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "prefix_pinned_sliding_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "prefix_pinned_sliding_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import prefix_pinned_sliding_amd"],
+                       cwd=str(tmp_path), capture_output=True, text=True, timeout=120,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libpsa.so" in r.stderr
