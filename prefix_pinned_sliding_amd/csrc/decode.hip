@@ -2,12 +2,13 @@
 // cross-split log-sum-exp merge (K3).
 //
 // [PS] 03: the query at t sees [1, P] and [max(P + 1, t - W + 1), t]. After the token at
-// p = n - 1 is appended, the cache holds exactly that set: prefix slots [0, min(n, P_b))
-// and the first min(W, n - P_b) ring slots. [PS] 06 skips every block of the evicted
-// middle; here the middle is never in memory, so the walk covers two contiguous slot
-// ranges and nothing else, and the only partially covered tile is the last one of a
-// split (masked per key). Softmax order does not matter, so the ring is walked in slot
-// order rather than age order.
+// p = n - 1 is appended, the cache holds exactly that set: the prefix slots in use and the
+// window's ring slots, which are contiguous modulo W from the window's head slot (the
+// whole ring once it is full; see SeqView). [PS] 06 skips every block of the evicted
+// middle; here the middle is never in memory, so the walk covers two slot ranges (the ring
+// one wrapping at most once) and nothing else, and the only partially covered tile is the
+// last one of a split (masked per key). Softmax order does not matter, so a full ring is
+// walked from slot 0 rather than in age order.
 //
 // Work split: one workgroup (4 waves) per (split, kv head, sequence). A split is a
 // contiguous run of `split_tokens` entries of the concatenated [prefix | ring] list.
