@@ -162,3 +162,19 @@ def test_import_fails_loudly_without_the_library(tmp_path):
                        env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libpsa.so" in r.stderr
+
+
+def test_counter_file_is_tied_to_kernel_code_not_comments(tmp_path):
+    # bench.py reports HBM traffic only while the decode kernel's code is the one the
+    # counters were taken on; a comment edit keeps the hash, a code edit changes it
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    src = open(bench.DECODE_SRC).read()
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text(src)
+    b.write_text("// a new comment\n" + src.replace("\n", "  // note\n", 3) + "\n\n")
+    c.write_text(src.replace("kRescaleSlack = 8.0f", "kRescaleSlack = 7.0f"))
+    assert bench.source_hash(str(a)) == bench.source_hash(str(b))
+    assert bench.source_hash(str(a)) != bench.source_hash(str(c))
