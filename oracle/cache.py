@@ -9,7 +9,7 @@ position base + i with base = max(P, n - W) ([KV-Lean] 2.4, 3.2).
 
 Stored bytes: V is stored exactly as given. K is stored rotated at its
 absolute position and rounded once to the storage dtype ([PS] 05: keys are
-rotated once and reused; the rounding is this build's reading, see `rne`).
+rotated once and reused; the single rounding is the reading taken here, see `rne`).
 """
 from __future__ import annotations
 
