@@ -13,6 +13,7 @@ namespace psa {
 namespace {
 
 constexpr int kBlock = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Storage element types: bf16 is kept as raw 16-bit patterns.
 template <int DT> struct Elem;
@@ -189,6 +190,55 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
     if (h == 0 && i == 0) c.tags[(size_t)b * c.S + slot] = p;
 }
 
+// Append of keys that are already rotated and rounded (a prefill chunk's staged keys) and
+// their values: the same slots, evictions and tags as append_kernel, moved 16 bytes at a
+// time. One thread per (sequence, token j, KV head, 16-byte chunk of a row).
+template <int DT, int D>
+__global__ __launch_bounds__(kBlock) void commit_kernel(DevCache c, const uint32_t* k,
+                                                        const uint32_t* v, int n_stride,
+                                                        const int32_t* __restrict__ len_cur,
+                                                        int32_t* __restrict__ len_next) {
+    using T = typename Elem<DT>::T;
+    constexpr int CPR = D * (int)sizeof(T) / 16;      // 16-byte chunks per row
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t total = (size_t)c.B * n_stride * c.Hkv * CPR;
+    if (idx >= total) return;
+    const int ch = (int)(idx % CPR);
+    size_t r = idx / CPR;
+    const int h = (int)(r % c.Hkv);
+    r /= c.Hkv;
+    const int j = (int)(r % n_stride);
+    const int b = (int)(r / n_stride);
+    const int nb = n_stride;
+    const int L0 = len_cur[b];
+    if (j == 0 && h == 0 && ch == 0) len_next[b] = L0 + nb;
+    const int p = L0 + j;
+    const int P = c.pre[b];
+    const int wf = c.wfloor[b], wl = c.wlen[b];
+    const int n1 = L0 + nb;
+    const int wb1 = max(wf, n1 - wl);
+    if (h == 0 && ch == 0 && wl < c.W) {                 // as in append_kernel
+        const int e = max(wf, L0 - wl) + j;
+        if (e < min(L0, wb1)) {
+            const int d = (wb1 - e) % c.W;
+            const int rel = d == 0 ? 0 : c.W - d;
+            if (rel >= n1 - wb1) c.tags[(size_t)b * c.S + c.Pmax + (e - P) % c.W] = -1;
+        }
+    }
+    int slot;
+    if (p < P) {
+        slot = p;
+    } else {
+        if (p < wb1) return;
+        slot = c.Pmax + (p - P) % c.W;
+    }
+    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * CPR + ch;
+    const size_t dst = (((size_t)b * c.Hkv + h) * c.S + slot) * CPR + ch;
+    reinterpret_cast<u32x4*>(c.k)[dst] = reinterpret_cast<const u32x4*>(k)[src];
+    reinterpret_cast<u32x4*>(c.v)[dst] = reinterpret_cast<const u32x4*>(v)[src];
+    if (h == 0 && ch == 0) c.tags[(size_t)b * c.S + slot] = p;
+}
+
 inline unsigned blocks_for(size_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
 
 }  // namespace
@@ -246,6 +296,21 @@ hipError_t launch_pool_load(const DevCache& c, int id, int len, const void* k, c
 
 hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_stride,
                          int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s) {
+    if (k_rotated && !ragged && n_uniform == n_stride &&
+        (((uintptr_t)k | (uintptr_t)v) & 15u) == 0) {
+        const int cpr = c.D * (c.dtype == PSA_BF16 ? 2 : 4) / 16;
+        const size_t total = (size_t)c.B * n_stride * c.Hkv * cpr;
+#define PSA_COMMIT(DT, DD)                                                                    \
+    hipLaunchKernelGGL((commit_kernel<DT, DD>), dim3(blocks_for(total)), dim3(kBlock), 0, s, c, \
+                       (const uint32_t*)k, (const uint32_t*)v, n_stride, c.len[cur], c.len[cur ^ 1])
+        if (c.dtype == PSA_BF16) {
+            if (c.D == 128) PSA_COMMIT(PSA_BF16, 128); else PSA_COMMIT(PSA_BF16, 64);
+        } else {
+            if (c.D == 128) PSA_COMMIT(PSA_F32, 128); else PSA_COMMIT(PSA_F32, 64);
+        }
+#undef PSA_COMMIT
+        return hipGetLastError();
+    }
     const size_t total = (size_t)c.B * n_stride * c.Hkv * (c.D / 2);
     const dim3 grid(blocks_for(total));
 #define PSA_APPEND(DT, DD)                                                                     \
