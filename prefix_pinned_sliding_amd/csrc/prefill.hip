@@ -14,16 +14,23 @@
 // masked element by element otherwise ([PS] 06: whole tiles in the evicted middle are never
 // loaded, partially covered tiles are masked).
 //
-// Per workgroup: 4 waves, 128 rows = (128 / G) positions x G query heads of one KV head, so
+// Per workgroup: 8 waves, 256 rows = (256 / G) positions x G query heads of one KV head, so
 // every K/V tile in LDS serves all G heads. Each wave owns 32 rows (two 16-row blocks).
 // Both products run on v_mfma_f32_16x16x32_bf16 in transposed form: S^T = K Q^T (K from
 // LDS as the A operand, Q^T held in registers as B) and O^T = V^T P^T (V^T from LDS, P^T
 // from registers). In S^T's accumulator layout each lane holds one row (query) and four
 // keys, which is exactly the B-operand layout P^T needs, so probabilities never leave
-// registers; row maxima need one cross-lane exchange per tile, row sums are reduced once
-// at the end. V is transposed into LDS while staging. Softmax runs on exp2 with the scale
-// folded into the staged queries; the running max is raised only when a tile exceeds it
-// by more than 2^8.
+// registers; row maxima need one cross-lane exchange per tile, row sums come from an MFMA
+// against ones. K and V are staged row-major; V^T operands are read with transposing LDS
+// loads. Softmax runs on exp2 with the scale folded into the staged queries; the running
+// max is raised only when a tile exceeds it by more than 2^8.
+//
+// Schedule: the waves form two groups of four, one wave of each on every SIMD. Group A
+// passes the tile's barrier after its PV products, group B right after its QK^T products,
+// so the groups run half a tile apart and one wave's softmax overlaps the other's matrix
+// products. Tiles go through three LDS buffers (tile N + 1 is written into tile N - 2's,
+// which both groups have left by then), with one barrier per tile; the next tile's K/V
+// are loaded into registers while the current one is computed.
 #include "psa_internal.h"
 #include "mfma_tile.h"
 #include "rope_round.h"
@@ -32,14 +39,17 @@ namespace psa {
 namespace {
 
 
-#ifndef PSA_PREFILL_PIPELINE
-#define PSA_PREFILL_PIPELINE 1   // 1: fetch the next tile's K/V while computing this one
-#endif
-
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                // staging kernel
 constexpr int kBlock = 64 * kWaves;
-constexpr int kRows = 128;              // rows (position x head) per workgroup
-constexpr int kBN = 64;                 // keys per tile
+constexpr int kPfWaves = 8;              // attention workgroup: two groups of 4 waves
+constexpr int kPfBlock = 64 * kPfWaves;
+constexpr int kRows = 32 * kPfWaves;     // rows (position x head) per workgroup
+constexpr int kBN = 64;                  // keys per tile
+constexpr int kNBuf = 3;                 // LDS tile buffers
+// LDS row strides (elements): K rows are read 16 bytes per lane, 8 rows per 128 bytes, so
+// a 4-bank offset between rows (D + 8) keeps them apart; V is read with transposing 8-byte
+// loads that take 4 rows x 32 bytes at once, which needs an 8-bank offset (D + 16).
+constexpr int kKPad = 8, kVPad = 16;
 
 // float64 -> bfloat16 for staged queries: the same single rounding as stored keys.
 __device__ __forceinline__ uint16_t q_to_bf16(double x) { return f64_to_bf16_bits(x); }
@@ -200,7 +210,7 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
 
 // Registers -> LDS: K and V rows as they are (consecutive lanes on consecutive 16-byte
 // chunks of a row); V^T operands are read back with transposing LDS loads.
-template <int D, int BN, int NT, int KSTR>
+template <int D, int BN, int NT, int KSTR, int VSTR>
 __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* v_s, int tid,
                                            const u32x4* kreg, const u32x4* vreg) {
     constexpr int CPR = D / 8;
@@ -210,7 +220,7 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* v_s, int tid
         const int ci = tid + NT * rr;
         const int kk = ci / CPR, col = ci % CPR;
         *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
-        *reinterpret_cast<u32x4*>(v_s + kk * KSTR + col * 8) = vreg[rr];
+        *reinterpret_cast<u32x4*>(v_s + kk * VSTR + col * 8) = vreg[rr];
     }
 }
 
@@ -234,33 +244,50 @@ template <int D>
 __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
                                           const uint16_t* k_s, const uint16_t* v_s,
                                           const int (&row_pos)[2], int ct0, int t1, int P, int W,
-                                          int l16, int lg, bool masked) {
+                                          int l16, int lg, bool masked, bool mid_barrier = false) {
     constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    constexpr int KSTR = D + 8;
+    constexpr int KSTR = D + kKPad, VSTR = D + kVPad;
     f32x4 s[2][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         s[0][kb] = f32x4{-st.mb[0], -st.mb[0], -st.mb[0], -st.mb[0]};
         s[1][kb] = f32x4{-st.mb[1], -st.mb[1], -st.mb[1], -st.mb[1]};
+    }
+    // k-step outer: the 8 accumulators are independent within a step, and the next step's
+    // K operands are read while this step's products run
+    bf16x8 ka[2][KB];
+    const uint16_t* kp = k_s + l16 * KSTR + 8 * lg;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = as_bf16x8(
-                *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
-            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[0][ks], s[0][kb], 0, 0, 0);
-            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[1][ks], s[1][kb], 0, 0, 0);
+    for (int kb = 0; kb < KB; ++kb)
+        ka[0][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kb * 16 * KSTR));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                ka[(ks + 1) & 1][kb] = as_bf16x8(
+                    *reinterpret_cast<const u32x4*>(kp + kb * 16 * KSTR + (ks + 1) * 32));
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[1][ks], s[1][kb], 0, 0, 0);
         }
     }
+    if (mid_barrier) __syncthreads();
     // Masked logits become -inf: exp2(-inf) is 0 for any finite shift.
     float ml[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         if (masked) {
             const int p = row_pos[rb];
+            int jb = ct0 + 4 * lg;
+            asm volatile("" : "+v"(jb));   // keeps the mask's arithmetic inside this branch
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int j = ct0 + kb * 16 + 4 * lg + i;
+                    const int j = jb + kb * 16 + i;
                     const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
                     s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
                 }
@@ -316,30 +343,31 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int ps = 0; ps < PVS; ++ps) {
-            const uint16_t* v0 = v_s + (32 * ps + 4 * lg + l16 / 4) * KSTR + db * 16 + 4 * (l16 % 4);
-            const bf16x8 a = lds_read_tr2(v0, v0 + 16 * KSTR);
+            const uint16_t* v0 = v_s + (32 * ps + 4 * lg + l16 / 4) * VSTR + db * 16 + 4 * (l16 % 4);
+            const bf16x8 a = lds_read_tr2(v0, v0 + 16 * VSTR);
             st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], st.o[0][db], 0, 0, 0);
             st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], st.o[1][db], 0, 0, 0);
         }
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
-                                                            uint16_t* __restrict__ out,
-                                                            float* __restrict__ lse, int chunk,
-                                                            int n_qtiles,
-                                                            const int32_t* __restrict__ len_cur) {
+__global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
+                                                              uint16_t* __restrict__ out,
+                                                              float* __restrict__ lse, int chunk,
+                                                              int n_qtiles,
+                                                              const int32_t* __restrict__ len_cur) {
     constexpr int BQ = kRows / G;         // positions per workgroup
     constexpr int KS = D / 32;            // k-steps of S^T = K Q^T
     constexpr int DB = D / 16;            // d-blocks of O^T
     constexpr int KB = kBN / 16;          // key blocks per tile
     constexpr int PVS = kBN / 32;         // k-steps of O^T = V^T P^T
-    constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
+    constexpr int KSTR = D + kKPad;       // LDS row strides (elements)
+    constexpr int VSTR = D + kVPad;
     constexpr int CPR = D / 8;            // 16-byte chunks per row
-    constexpr int KLD = (kBN * CPR) / kBlock;
+    constexpr int KLD = (kBN * CPR) / kPfBlock;
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[kNBuf][kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_s[kNBuf][kBN * VSTR];
 
     // XCD-aware tile order: workgroup L runs on XCD L % 8; give each XCD a contiguous run
     // of logical tiles so all query tiles of one (sequence, KV head) share that XCD's L2.
@@ -414,33 +442,51 @@ __global__ __launch_bounds__(kBlock, 2) void prefill_kernel(DevCache c, const ui
 
     u32x4 kreg[KLD], vreg[KLD];
     int seg = 0, t0 = -kBN;
-    bool have = walk_next<kBN>(wk, seg, t0);
-    if (PSA_PREFILL_PIPELINE && have)
-        fetch_tile<D, kBN, kBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
-#pragma unroll 1
-    while (have) {
-        const int cseg = seg, ct0 = t0;
-        if (q_prefix && cseg >= 2) {
-            const uint16_t* sq = (const uint16_t*)c.stage_q;
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(sq + q_off[rb] + ks * 32));
-            q_prefix = false;
-        }
-        const int t1 = min(ct0 + kBN, wk.hi(cseg));
-        const bool full = (ct0 + kBN == t1) && (t1 - 1 <= p_lo) &&
-                          (t1 - 1 < P || ct0 >= p_hi - W + 1);
-        __syncthreads();                  // the previous tile's LDS reads are done
-        if (!PSA_PREFILL_PIPELINE) fetch_tile<D, kBN, kBlock>(src, cseg, ct0, t1, tid, kreg, vreg);
-        stage_tile<D, kBN, kBlock, KSTR>(k_s, v_s, tid, kreg, vreg);
-        have = walk_next<kBN>(wk, seg, t0);
-        if (PSA_PREFILL_PIPELINE && have)   // in flight while this tile is computed
-            fetch_tile<D, kBN, kBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+    // Two groups of waves, A (waves 0 .. kPfWaves/2 - 1) and B (the rest), each SIMD holding
+    // one wave of each. A passes the tile's barrier after its PV products, B after its QK^T
+    // products, so on every SIMD one wave's softmax overlaps the other wave's products.
+    // Three LDS buffers: tile N + 1 is written (by every wave, after barrier N - 1) into the
+    // buffer of tile N - 2, which both groups have finished reading by then. The walk is the
+    // same for every wave of the workgroup, so all waves pass the same number of barriers:
+    // one before the loop and one per tile.
+    const bool grp_b = __builtin_amdgcn_readfirstlane(wave) >= kPfWaves / 2;
+    if (walk_next<kBN>(wk, seg, t0)) {
+        int cseg = seg, ct0 = t0, cur = 0;
+        fetch_tile<D, kBN, kPfBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+        stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
+        bool have = walk_next<kBN>(wk, seg, t0);
+        if (have) fetch_tile<D, kBN, kPfBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
         __syncthreads();
-
-        tile_step<D>(st, qop, k_s, v_s, row_pos, ct0, t1, P, W, l16, lg, !full);
+#pragma unroll 1
+        while (true) {
+            const int nseg = seg, nt0 = t0;
+            const int nxt = cur == 2 ? 0 : cur + 1;
+            bool have_next = false;
+            if (have) {
+                stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
+                have_next = walk_next<kBN>(wk, seg, t0);
+                if (have_next) fetch_tile<D, kBN, kPfBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+            }
+            if (q_prefix && cseg >= 2) {
+                const uint16_t* sq = (const uint16_t*)c.stage_q;
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(sq + q_off[rb] + ks * 32));
+                q_prefix = false;
+            }
+            const int t1 = min(ct0 + kBN, wk.hi(cseg));
+            const bool full = (ct0 + kBN == t1) && (t1 - 1 <= p_lo) &&
+                              (t1 - 1 < P || ct0 >= p_hi - W + 1);
+            tile_step<D>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, t1, P, W, l16, lg, !full, grp_b);
+            if (!grp_b) __syncthreads();
+            if (!have) break;
+            cseg = nseg;
+            ct0 = nt0;
+            have = have_next;
+            cur = nxt;
+        }
     }
 
     // ---- normalise and write -------------------------------------------------------------
@@ -474,7 +520,7 @@ hipError_t launch_g(const DevCache& c, const void* v, void* out, float* lse, int
     const int n_qtiles = (chunk + BQ - 1) / BQ;
     const int total = n_qtiles * c.Hkv * c.B;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(grid), dim3(kBlock), 0, s, c,
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(grid), dim3(kPfBlock), 0, s, c,
                        (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
     return hipGetLastError();
 }
