@@ -86,7 +86,11 @@ typedef struct {
     int32_t n_shared_prefixes; /* >= 0: entries of the shared-prefix pool */
     int32_t shared_prefix_max; /* >= 0: longest prefix one pool entry holds */
     int32_t pe_mode;     /* PSA_PE_CONTINUE or PSA_PE_RESET */
-    int32_t reserved;    /* must be 0 */
+    int32_t block_size;  /* 0: contiguous slots per sequence; else paged K/V (see psa_layout):
+                            a power of two >= 16 that divides prefix_max and window, with
+                            (prefix_max + window) / block_size <= 1024 */
+    int32_t n_blocks;    /* paged only: physical blocks in the pool (0 selects
+                            max_batch * (prefix_max + window) / block_size); else 0 */
 } psa_cache_desc;
 
 /* Position encoding of attended tokens ([PS] 05).
@@ -101,10 +105,23 @@ typedef struct {
 enum { PSA_PE_CONTINUE = 0, PSA_PE_RESET = 1 };
 
 /* Byte offsets of the regions the library carves out of the caller's device buffer.
- * K and V: [B][H_kv][S][D] with S = prefix_max + window slots per (sequence, head):
- * slots [0, P_max) hold prefix positions p < P_b at slot p (promoted entries follow at
- * slots P_b, P_b + 1, ...); slots [P_max, S) are the ring, position p >= P_b at slot
- * P_max + (p - P_b) mod W.
+ * Every sequence has S = prefix_max + window logical slots: slots [0, P_max) hold prefix
+ * positions p < P_b at slot p (promoted entries follow at slots P_b, P_b + 1, ...);
+ * slots [P_max, S) are the ring, position p >= P_b at slot P_max + (p - P_b) mod W.
+ * K and V, contiguous (block_size 0): [B][H_kv][S][D], slot s of (b, h) at row
+ * (b * H_kv + h) * S + s.
+ * K and V, paged ([KV-Lean] 6.1: the logical cache read through a table of physical
+ * blocks): [H_kv][n_blocks][block_size][D]; the block table [B][S / block_size] int32
+ * (at btab_offset) maps logical block s / block_size of sequence b to a physical block,
+ * -1 if none, and slot s of (b, h) is row (h * n_blocks + blk) * block_size + s % block_size.
+ * (Head-major, so the blocks a sequence takes one after another form one contiguous run per
+ * head.)
+ * The library owns the table: a block is taken from the pool when a call first writes
+ * one of its slots (append, prefill, promotion) and returned when the sequence is reset
+ * or attached; a window that has filled its ring reuses its blocks. A sequence holds
+ * ceil(pinned entries / block_size) prefix blocks (none when attached to a shared
+ * prefix) plus the ring blocks its window positions have touched, at most
+ * window / block_size.
  * tags: [B][S] int32, the absolute position held by each slot, -1 if it holds no cached
  * entry (never written, or its entry left the cache without being overwritten).
  * pool K and V: [n_shared_prefixes][H_kv][shared_prefix_max][D], position p of entry e
@@ -115,11 +132,14 @@ typedef struct {
     size_t pool_k_offset;
     size_t pool_v_offset;
     size_t tags_offset;
+    size_t btab_offset;   /* paged: block table [B][S / block_size] int32 */
     size_t state_offset;  /* library-private per-sequence state */
     size_t work_offset;   /* library-private workspace */
     size_t total_bytes;   /* == psa_cache_bytes() */
     int32_t slots;        /* S */
     int32_t elem_bytes;   /* 2 (bf16) or 4 (f32) */
+    int32_t block_size;   /* 0 (contiguous) or the block size */
+    int32_t n_blocks;     /* paged: physical blocks in the pool */
 } psa_layout;
 
 /* Device bytes the caller must provide for a cache described by *desc (0 if *desc is
@@ -183,9 +203,17 @@ int psa_seq_set_window(psa_cache *cache, int32_t seq, int32_t window, psa_stream
  * where they stay for good (their keys keep the rotation of their absolute positions;
  * they are copied to the next free prefix slots). Errors: PSA_ERR_ARG if count is
  * negative, exceeds the window's entries, or the pinned list would exceed prefix_max;
- * PSA_ERR_STATE if `seq` was never reset, reads a shared prefix (psa_seq_attach), or the
- * cache uses PSA_PE_RESET (renumbered positions are defined for [prefix, window] only). */
+ * PSA_ERR_STATE if `seq` was never reset, reads a shared prefix (psa_seq_attach), the
+ * cache uses PSA_PE_RESET (renumbered positions are defined for [prefix, window] only),
+ * or (paged) no free block is left for the prefix slots. */
 int psa_seq_promote(psa_cache *cache, int32_t seq, int32_t count, psa_stream stream);
+
+/* Paged caches: copy sequence `seq`'s block table (S / block_size entries, physical block
+ * or -1) into table_host (may be NULL) and its length into *entries; *free_blocks (may be
+ * NULL) receives the pool's unused blocks. Host only. Errors: PSA_ERR_ARG for a
+ * contiguous cache or a NULL `entries`; PSA_ERR_STATE if `seq` is out of range. */
+int psa_seq_blocks(const psa_cache *cache, int32_t seq, int32_t *table_host, int32_t *entries,
+                   int32_t *free_blocks);
 
 /* From the host mirror: the sequence's window length, its pinned entries (min(n, P_b)
  * plus promoted ones) and its window entries; any output may be NULL. Host only.
@@ -202,8 +230,9 @@ int psa_seq_window(const psa_cache *cache, int32_t seq, int32_t *window, int32_t
  * overwriting (evicting) position p - W; with w_b < W the window's oldest entries leave
  * by the length rule and their slots get tag -1. The key is stored rotated at p. A token
  * that a later token of the same call evicts is not written.
- * Errors: PSA_ERR_STATE if a sequence with n_b > 0 was never reset;
- * PSA_ERR_OVERFLOW if len_b + n_b > INT32_MAX. */
+ * Errors: PSA_ERR_STATE if a sequence with n_b > 0 was never reset, or (paged) if the
+ * pool has fewer free blocks than the call needs; PSA_ERR_OVERFLOW if
+ * len_b + n_b > INT32_MAX. */
 int psa_append(psa_cache *cache, const int32_t *n_new_host, int32_t n_uniform, const void *k,
                const void *v, int32_t n_stride, psa_stream stream);
 
@@ -220,7 +249,8 @@ int psa_decode_attn(psa_cache *cache, const void *q, void *out, float *lse, psa_
  * consecutive decode steps). Then the chunk is appended as by psa_append.
  * q, out: [B][chunk][H_q][D]; k, v: [B][chunk][H_kv][D]; lse: [B][chunk][H_q] float32
  * or NULL. 1 <= chunk <= max_chunk. Errors: PSA_ERR_STATE if a sequence was never
- * reset; PSA_ERR_OVERFLOW as psa_append. */
+ * reset or (paged) the pool has fewer free blocks than the chunk needs;
+ * PSA_ERR_OVERFLOW as psa_append. */
 int psa_prefill_attn(psa_cache *cache, int32_t chunk, const void *q, const void *k,
                      const void *v, void *out, float *lse, psa_stream stream);
 

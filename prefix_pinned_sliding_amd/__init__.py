@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -43,7 +43,8 @@ class Desc(ctypes.Structure):
         ("n_shared_prefixes", ctypes.c_int32),
         ("shared_prefix_max", ctypes.c_int32),
         ("pe_mode", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
     ]
 
 
@@ -55,11 +56,14 @@ class Layout(ctypes.Structure):
         ("pool_k_offset", ctypes.c_size_t),
         ("pool_v_offset", ctypes.c_size_t),
         ("tags_offset", ctypes.c_size_t),
+        ("btab_offset", ctypes.c_size_t),
         ("state_offset", ctypes.c_size_t),
         ("work_offset", ctypes.c_size_t),
         ("total_bytes", ctypes.c_size_t),
         ("slots", ctypes.c_int32),
         ("elem_bytes", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
     ]
 
 
@@ -94,6 +98,7 @@ def _load() -> ctypes.CDLL:
         "psa_seq_promote": (ctypes.c_int, [P, I32, I32, P]),
         "psa_seq_window": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                           ctypes.POINTER(I32)]),
+        "psa_seq_blocks": (ctypes.c_int, [P, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "psa_append": (ctypes.c_int, [P, P, I32, P, P, I32, P]),
         "psa_decode_attn": (ctypes.c_int, [P, P, P, P, P]),
         "psa_prefill_attn": (ctypes.c_int, [P, I32, P, P, P, P, P, P]),
@@ -139,14 +144,15 @@ def _ptr(t: Optional[torch.Tensor]):
 def make_desc(max_batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, prefix_max: int,
               window: int, dtype: torch.dtype = torch.bfloat16, rope_base: float = 10000.0,
               scale: float = 0.0, max_chunk: int = 0, n_shared_prefixes: int = 0,
-              shared_prefix_max: int = 0, pe: str = "continue") -> Desc:
+              shared_prefix_max: int = 0, pe: str = "continue", block_size: int = 0,
+              n_blocks: int = 0) -> Desc:
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {dtype}")
     if pe not in _PE:
         raise ValueError(f"pe must be one of {list(_PE)}")
     return Desc(max_batch, n_q_heads, n_kv_heads, head_dim, prefix_max, window, _DTYPES[dtype],
                 max_chunk, float(rope_base), float(scale), n_shared_prefixes, shared_prefix_max,
-                _PE[pe], 0)
+                _PE[pe], block_size, n_blocks)
 
 
 def cache_bytes(desc: Desc) -> int:
@@ -175,10 +181,11 @@ class Cache:
                  prefix_max: int, window: int, dtype: torch.dtype = torch.bfloat16,
                  rope_base: float = 10000.0, scale: float = 0.0, max_chunk: int = 0,
                  device=None, stream=None, n_shared_prefixes: int = 0, shared_prefix_max: int = 0,
-                 pe: str = "continue"):
+                 pe: str = "continue", block_size: int = 0, n_blocks: int = 0):
         self.desc = make_desc(max_batch, n_q_heads, n_kv_heads, head_dim, prefix_max, window,
                               dtype, rope_base, scale, max_chunk, n_shared_prefixes,
-                              shared_prefix_max, pe)
+                              shared_prefix_max, pe, block_size, n_blocks)
+        self.block_size = block_size
         self.pe = pe
         self.n_shared, self.shared_max = n_shared_prefixes, shared_prefix_max
         self.dtype = dtype
@@ -210,12 +217,26 @@ class Cache:
             .view(torch.int32).view(self.B, S)
 
     def raw_kv(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        """K and V storage: [B][H_kv][S][D], or [H_kv][n_blocks][block_size][D] when paged."""
         S, e = self.layout.slots, self.layout.elem_bytes
-        n = self.B * self.Hkv * S * self.D * e
+        if self.block_size:
+            shape = (self.Hkv, self.layout.n_blocks, self.block_size, self.D)
+        else:
+            shape = (self.B, self.Hkv, S, self.D)
+        n = shape[0] * shape[1] * shape[2] * shape[3] * e
         k = self.mem[self.layout.k_offset:self.layout.k_offset + n].view(self.dtype)
         v = self.mem[self.layout.v_offset:self.layout.v_offset + n].view(self.dtype)
-        shape = (self.B, self.Hkv, S, self.D)
         return k.view(shape), v.view(shape)
+
+    def blocks(self, seq: int) -> Tuple[List[int], int]:
+        """Paged caches: (block table of `seq`, one physical block or -1 per logical block;
+        free blocks in the pool), from the host's allocator."""
+        nb = self.layout.slots // self.block_size if self.block_size else 0
+        table = (ctypes.c_int32 * max(nb, 1))()
+        n, free = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.psa_seq_blocks(self._h, seq, table, ctypes.byref(n), ctypes.byref(free)),
+               "psa_seq_blocks")
+        return list(table[:n.value]), free.value
 
     # -- calls ---------------------------------------------------------------------------
     def reset(self, seq: int, prefix_len: int, stream=None) -> None:

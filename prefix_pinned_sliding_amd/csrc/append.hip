@@ -26,13 +26,21 @@ __device__ __forceinline__ double to_f64(float f) { return (double)f; }
 __device__ __forceinline__ uint16_t store_as(double x, uint16_t*) { return f64_to_bf16_bits(x); }
 __device__ __forceinline__ float store_as(double x, float*) { return (float)x; }
 
-// Tags -1; lengths, prefix lengths and token counts 0; prefix entries -1 (own prefix).
+// Tags -1; lengths, prefix lengths and token counts 0; prefix entries -1 (own prefix);
+// block-table entries -1 (paged).
 __global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_zero,
-                            int32_t* pid, int B) {
+                            int32_t* pid, int B, int32_t* btab, size_t n_btab) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_tags) tags[i] = -1;
     if (i < (size_t)n_zero) state[i] = 0;
     if (i < (size_t)B) pid[i] = -1;
+    if (i < n_btab) btab[i] = -1;
+}
+
+// Paged: block-table entries chosen by the host's block allocator.
+__global__ void table_update_kernel(int32_t* btab, TableUpdate u) {
+    const int i = threadIdx.x;
+    if (i < u.n) btab[u.idx[i]] = u.blk[i];
 }
 
 // A new sequence pins its first prefix_len tokens and uses the full window length W.
@@ -40,6 +48,7 @@ __global__ void seq_reset_kernel(DevCache c, int32_t* len_cur, int seq, int pref
                                  int prefix_id) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < c.S) c.tags[(size_t)seq * c.S + i] = -1;
+    if (i < c.NBT) c.btab[(size_t)seq * c.NBT + i] = -1;   // paged: blocks go back to the pool
     if (i == 0) {
         len_cur[seq] = len0;
         c.pre[seq] = prefix_len;
@@ -77,11 +86,11 @@ __global__ __launch_bounds__(kBlock) void promote_kernel(DevCache c, int seq, in
     const int p = wb + j;
     const int from = c.Pmax + (p - c.pre[seq]) % c.W;
     const int to = npin + j;
-    const size_t head = ((size_t)seq * c.Hkv + h) * c.S;
+    const size_t rf = kv_rowidx(c, seq, h, from), rt = kv_rowidx(c, seq, h, to);
     uint32_t* K = (uint32_t*)c.k;
     uint32_t* V = (uint32_t*)c.v;
-    K[(head + to) * row_words + w] = K[(head + from) * row_words + w];
-    V[(head + to) * row_words + w] = V[(head + from) * row_words + w];
+    K[rt * row_words + w] = K[rf * row_words + w];
+    V[rt * row_words + w] = V[rf * row_words + w];
     if (h == 0 && w == 0) {
         c.tags[(size_t)seq * c.S + to] = p;
         c.tags[(size_t)seq * c.S + from] = -1;
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
         slot = c.Pmax + (p - P) % c.W;
     }
     const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * D;
-    const size_t dst = (((size_t)b * c.Hkv + h) * c.S + slot) * D;
+    const size_t dst = kv_rowidx(c, b, h, slot) * D;
     T* K = (T*)c.k;
     T* V = (T*)c.v;
     if (k_rotated) {
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(DevCache c, const uint32
         slot = c.Pmax + (p - P) % c.W;
     }
     const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * CPR + ch;
-    const size_t dst = (((size_t)b * c.Hkv + h) * c.S + slot) * CPR + ch;
+    const size_t dst = kv_rowidx(c, b, h, slot) * CPR + ch;
     reinterpret_cast<u32x4*>(c.k)[dst] = reinterpret_cast<const u32x4*>(k)[src];
     reinterpret_cast<u32x4*>(c.v)[dst] = reinterpret_cast<const u32x4*>(v)[src];
     if (h == 0 && ch == 0) c.tags[(size_t)b * c.S + slot] = p;
@@ -248,8 +257,16 @@ hipError_t launch_init(const DevCache& c, hipStream_t s) {
     const int n_zero = 4 * c.B;   // len[0], len[1], pre, nnew are contiguous; the rest is set
                                   // by the reset of each sequence
     const size_t n = n_tags > (size_t)n_zero ? n_tags : (size_t)n_zero;
-    hipLaunchKernelGGL(init_kernel, dim3(blocks_for(n)), dim3(kBlock), 0, s, c.tags, n_tags,
-                       c.len[0], n_zero, c.pid, c.B);
+    const size_t n_btab = (size_t)c.B * c.NBT;
+    const size_t m = n > n_btab ? n : n_btab;
+    hipLaunchKernelGGL(init_kernel, dim3(blocks_for(m)), dim3(kBlock), 0, s, c.tags, n_tags,
+                       c.len[0], n_zero, c.pid, c.B, c.btab, n_btab);
+    return hipGetLastError();
+}
+
+hipError_t launch_table_update(const DevCache& c, const TableUpdate& u, hipStream_t s) {
+    if (u.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(table_update_kernel, dim3(1), dim3(kTableUpdates), 0, s, c.btab, u);
     return hipGetLastError();
 }
 

@@ -126,7 +126,7 @@ struct KVTile {
     u32x4 k[U][CPL], v[U][CPL];
 };
 
-template <int DT, int D, int G, int LPK>
+template <int DT, int D, int G, int LPK, bool PAGED>
 __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
                                                                 const typename Elem<DT>::T* q,
                                                                 int split_tokens,
@@ -187,18 +187,39 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     const T* Kr = (const T*)c.k + head_off + (size_t)c.Pmax * D;
     const T* Vr = (const T*)c.v + head_off + (size_t)c.Pmax * D;
 
+    // Paged: the sequence's block table, read once into LDS.
+    __shared__ int32_t tab_s[PAGED ? kMaxBlockTable : 1];
+    if constexpr (PAGED) {
+        for (int j = tid; j < c.NBT; j += kBlock) tab_s[j] = c.btab[(size_t)b * c.NBT + j];
+        __syncthreads();
+    }
+
     // Logical entry i -> physical row: the prefix rows, then the window's ring rows from
     // ring_head on, wrapping once. Attention does not depend on the order of its keys, so
-    // a full ring is read from slot 0.
+    // a full ring is read from slot 0. Paged, logical slot s of the sequence is row
+    // s mod Bs of block tab_s[s / Bs] (prefix rows of a shared prefix stay in the pool).
     auto load = [&](Tile& t, int base_i) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = min(base_i + u * KPW + grp, i1 - 1);
             const bool pre = i < n_pre;
             const int rr = i - n_pre + ring_head;
-            const size_t row = (size_t)(pre ? i : (rr >= c.W ? rr - c.W : rr)) * D;
-            const u32x4* kp = reinterpret_cast<const u32x4*>((pre ? Kp : Kr) + row);
-            const u32x4* vp = reinterpret_cast<const u32x4*>((pre ? Vp : Vr) + row);
+            const int ring_row = rr >= c.W ? rr - c.W : rr;
+            const u32x4* kp;
+            const u32x4* vp;
+            if constexpr (PAGED) {
+                const int slot = pre ? i : c.Pmax + ring_row;
+                const bool pool = pre && pid >= 0;
+                const size_t row = pool ? (size_t)i * D
+                                        : block_rowidx(tab_s[slot >> c.bshift], h, slot & (c.Bs - 1),
+                                                       c.Bs, c.n_blocks) * D;
+                kp = reinterpret_cast<const u32x4*>((pool ? Kp : (const T*)c.k) + row);
+                vp = reinterpret_cast<const u32x4*>((pool ? Vp : (const T*)c.v) + row);
+            } else {
+                const size_t row = (size_t)(pre ? i : ring_row) * D;
+                kp = reinterpret_cast<const u32x4*>((pre ? Kp : Kr) + row);
+                vp = reinterpret_cast<const u32x4*>((pre ? Vp : Vr) + row);
+            }
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 t.k[u][cc] = __builtin_nontemporal_load(kp + cc * LPK + sub);
@@ -379,8 +400,12 @@ hipError_t launch_partial_g(const DevCache& c, const void* q, int split_tokens, 
     constexpr int PREF = G <= 2 ? PSA_DECODE_LPK_G2 : (G == 4 ? 8 : 16);
     constexpr int LPK = PREF < CPR ? PREF : CPR;
     const dim3 grid(grid_splits, c.Hkv, c.B);
-    hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK>), grid, dim3(kBlock), 0, s, c,
-                       (const typename Elem<DT>::T*)q, split_tokens, c.len[cur]);
+    if (c.Bs > 0)
+        hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK, true>), grid, dim3(kBlock), 0, s, c,
+                           (const typename Elem<DT>::T*)q, split_tokens, c.len[cur]);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK, false>), grid, dim3(kBlock), 0, s, c,
+                           (const typename Elem<DT>::T*)q, split_tokens, c.len[cur]);
     return hipGetLastError();
 }
 
@@ -405,7 +430,7 @@ int wgs_per_cu_g() {
     if (cached == 0) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void*>(&decode_partial_kernel<DT, D, G, LPK>), kBlock,
+                &n, reinterpret_cast<const void*>(&decode_partial_kernel<DT, D, G, LPK, false>), kBlock,
                 0) != hipSuccess || n < 1)
             n = 1;
         cached = n;

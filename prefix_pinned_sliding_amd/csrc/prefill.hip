@@ -161,6 +161,9 @@ struct TileSrc {
     const uint16_t *k_prefix, *v_prefix;   // own prefix slots or the shared-prefix entry
     size_t chunk_row0;   // b * chunk
     int n, P, W, Pmax, Hkv, h;             // P: P_b (ring origin), W: ring slots
+    const int32_t* tab;                    // paged: the sequence's block table (LDS)
+    int Bs, bshift, nblk;
+    bool pool_prefix;                      // prefix rows come from the shared-prefix pool
 };
 
 // This thread's share of a tile into registers: KLD 16-byte chunks of K rows (lanes along
@@ -168,12 +171,31 @@ struct TileSrc {
 // read the last valid row (masked later). Each tile gets one base pointer per operand;
 // rows are 32-bit offsets from it: consecutive rows for the prefix and the chunk, the ring
 // slot (reduced modulo W once per tile, then one wrap) for the window.
-template <int D, int BN, int NT>
+template <int D, int BN, int NT, bool PAGED>
 __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, int t1, int tid,
                                            u32x4* kreg, u32x4* vreg) {
     constexpr int CPR = D / 8;
     constexpr int KLD = (BN * CPR) / NT;
     const int last = t1 - 1 - t0;
+    if (PAGED && (seg == 2 || (seg == 0 && !s.pool_prefix))) {
+        // paged cache rows: logical slot -> row of its physical block, row by row
+        const int ring0 = seg == 2 ? (t0 - s.P) % s.W : 0;
+#pragma unroll
+        for (int rr = 0; rr < KLD; ++rr) {
+            const int ci = tid + NT * rr;
+            const int kk = min(ci / CPR, last), col = ci % CPR;
+            int slot = t0 + kk;
+            if (seg == 2) {
+                const int r = ring0 + kk;
+                slot = s.Pmax + (r >= s.W ? r - s.W : r);
+            }
+            const size_t e = block_rowidx(s.tab[slot >> s.bshift], s.h, slot & (s.Bs - 1), s.Bs,
+                                          s.nblk) * D + col * 8;
+            kreg[rr] = *reinterpret_cast<const u32x4*>(s.k_cache + e);
+            vreg[rr] = *reinterpret_cast<const u32x4*>(s.v_cache + e);
+        }
+        return;
+    }
     const uint16_t* kb;
     const uint16_t* vb;
     int stride, ring0 = 0;
@@ -350,7 +372,7 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
         }
 }
 
-template <int D, int G>
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
                                                               uint16_t* __restrict__ out,
                                                               float* __restrict__ lse, int chunk,
@@ -434,11 +456,19 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     const Walk wk{nA, n, hi1, lo2, n, lo3, p_hi + 1, P, p_lo - W + 1};
     const int pid = c.pid[b];
     const size_t pre_off = pid >= 0 ? ((size_t)pid * c.Hkv + h) * (size_t)c.shared_max * D : head_off;
-    const TileSrc src{(const uint16_t*)c.k + head_off, (const uint16_t*)c.v + head_off,
+    // Paged: the sequence's block table in LDS; cache rows are addressed from the pool base.
+    __shared__ int32_t tab_s[PAGED ? kMaxBlockTable : 1];
+    if constexpr (PAGED) {
+        for (int j = tid; j < c.NBT; j += kPfBlock) tab_s[j] = c.btab[(size_t)b * c.NBT + j];
+        __syncthreads();
+    }
+    const size_t cache_off = PAGED ? 0 : head_off;
+    const TileSrc src{(const uint16_t*)c.k + cache_off, (const uint16_t*)c.v + cache_off,
                       (const uint16_t*)c.stage_k, v_in,
                       (const uint16_t*)(pid >= 0 ? c.pool_k : c.k) + pre_off,
                       (const uint16_t*)(pid >= 0 ? c.pool_v : c.v) + pre_off,
-                      (size_t)b * chunk, n, c.pre[b], c.W, c.Pmax, c.Hkv, h};
+                      (size_t)b * chunk, n, c.pre[b], c.W, c.Pmax, c.Hkv, h,
+                      tab_s, c.Bs, c.bshift, c.n_blocks, pid >= 0};
 
     u32x4 kreg[KLD], vreg[KLD];
     int seg = 0, t0 = -kBN;
@@ -452,10 +482,10 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     const bool grp_b = __builtin_amdgcn_readfirstlane(wave) >= kPfWaves / 2;
     if (walk_next<kBN>(wk, seg, t0)) {
         int cseg = seg, ct0 = t0, cur = 0;
-        fetch_tile<D, kBN, kPfBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+        fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
         stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
         bool have = walk_next<kBN>(wk, seg, t0);
-        if (have) fetch_tile<D, kBN, kPfBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+        if (have) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
         __syncthreads();
 #pragma unroll 1
         while (true) {
@@ -465,7 +495,7 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
             if (have) {
                 stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
                 have_next = walk_next<kBN>(wk, seg, t0);
-                if (have_next) fetch_tile<D, kBN, kPfBlock>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+                if (have_next) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
             }
             if (q_prefix && cseg >= 2) {
                 const uint16_t* sq = (const uint16_t*)c.stage_q;
@@ -520,8 +550,12 @@ hipError_t launch_g(const DevCache& c, const void* v, void* out, float* lse, int
     const int n_qtiles = (chunk + BQ - 1) / BQ;
     const int total = n_qtiles * c.Hkv * c.B;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(grid), dim3(kPfBlock), 0, s, c,
-                       (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
+    if (c.Bs > 0)
+        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(grid), dim3(kPfBlock), 0, s, c,
+                           (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(grid), dim3(kPfBlock), 0, s, c,
+                           (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
     return hipGetLastError();
 }
 

@@ -46,6 +46,8 @@ struct psa_cache {
     std::vector<int32_t> wlen;     // window length per sequence
     std::vector<int32_t> pool_len; // tokens held by each pool entry, -1 = never loaded
     std::vector<int32_t> attached; // sequences attached to each pool entry
+    std::vector<int32_t> btab;     // paged: host copy of the block table [B][NBT]
+    std::vector<int32_t> free_blk; // paged: unused physical blocks (a stack)
     int32_t split_tokens;          // 0 = automatic
     int resident_wgs;              // decode workgroups resident at once (0 = not yet queried)
     bool profiling;
@@ -81,9 +83,21 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     if ((int64_t)d.shared_prefix_max + d.window > (1 << 30)) return bad("shared_prefix_max too large");
     if (d.pe_mode != PSA_PE_CONTINUE && d.pe_mode != PSA_PE_RESET)
         return bad("pe_mode must be PSA_PE_CONTINUE or PSA_PE_RESET");
-    if (d.reserved != 0) return bad("reserved must be 0");
     const int64_t S = (int64_t)d.prefix_max + d.window;
     if (S > (1 << 30)) return bad("prefix_max + window too large");
+    int64_t n_blocks = 0;
+    if (d.block_size != 0) {
+        const int bs = d.block_size;
+        if (bs < 16 || (bs & (bs - 1)) != 0) return bad("block_size must be 0 or a power of two >= 16");
+        if (d.prefix_max % bs != 0 || d.window % bs != 0)
+            return bad("block_size must divide prefix_max and window");
+        if (S / bs > kMaxBlockTable) return bad("(prefix_max + window) / block_size must be <= 1024");
+        if (d.n_blocks < 0) return bad("n_blocks must be >= 0");
+        n_blocks = d.n_blocks > 0 ? d.n_blocks : (int64_t)d.max_batch * (S / bs);
+        if (n_blocks > (1 << 30)) return bad("n_blocks too large");
+    } else if (d.n_blocks != 0) {
+        return bad("n_blocks must be 0 for a contiguous cache");
+    }
     const size_t elem = d.dtype == PSA_BF16 ? 2 : 4;
     const size_t B = (size_t)d.max_batch, Hq = (size_t)d.n_q_heads, Hkv = (size_t)d.n_kv_heads;
     const size_t D = (size_t)d.head_dim;
@@ -91,12 +105,15 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     const int64_t max_splits = (S + kSplitGranule - 1) / kSplitGranule + 1;
     const size_t A = 256;
     size_t off = 0;
-    L->k = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
-    L->v = off;        off = align_up(off + B * Hkv * (size_t)S * D * elem, A);
+    const size_t kv_rows = d.block_size ? (size_t)n_blocks * Hkv * (size_t)d.block_size
+                                        : B * Hkv * (size_t)S;
+    L->k = off;        off = align_up(off + kv_rows * D * elem, A);
+    L->v = off;        off = align_up(off + kv_rows * D * elem, A);
     const size_t pool = (size_t)d.n_shared_prefixes * Hkv * (size_t)d.shared_prefix_max * D * elem;
     L->pool_k = off;   off = align_up(off + pool, A);
     L->pool_v = off;   off = align_up(off + pool, A);
     L->tags = off;     off = align_up(off + B * (size_t)S * 4, A);
+    L->btab = off;     off = align_up(off + (d.block_size ? B * (size_t)(S / d.block_size) * 4 : 0), A);
     L->state = off;    off = align_up(off + 8 * B * 4, A);
     L->inv_freq = off; off = align_up(off + D / 2 * 8, A);
     L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
@@ -109,6 +126,7 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     L->S = (int32_t)S;
     L->elem = (int32_t)elem;
     L->max_splits = (int32_t)max_splits;
+    L->n_blocks = (int32_t)n_blocks;
     return true;
 }
 
@@ -174,6 +192,119 @@ int auto_split_tokens(psa_cache* c) {
 
 bool valid_seq(const psa_cache* c, int32_t seq) { return seq >= 0 && seq < c->desc.max_batch; }
 
+// ---- paged caches: the host's block allocator -------------------------------------------
+// Logical block j of sequence b covers slots [j * Bs, (j + 1) * Bs); the device table gets
+// an entry when a call is about to write one of those slots for the first time.
+
+// Logical blocks written when sequence b appends positions [n0, n1): prefix slots for
+// p < P_b, ring slots (p - P_b) mod W otherwise (every ring block once n1 - n0 >= W; tokens
+// dropped again within the call are counted too, which only maps a block early).
+void blocks_of_positions(const psa_cache* c, int b, int64_t n0, int64_t n1, std::vector<int>& out) {
+    const int Bs = c->dev.Bs, W = c->dev.W, Pmax = c->dev.Pmax;
+    const int64_t P = c->pre[b];
+    const int64_t pe = n1 < P ? n1 : P;
+    for (int64_t p = n0; p < pe; p = (p / Bs + 1) * Bs) out.push_back((int)(p / Bs));
+    const int64_t lo = n0 > P ? n0 : P;
+    if (n1 <= lo) return;
+    const int64_t count = n1 - lo;
+    if (count >= W) {
+        for (int j = Pmax / Bs; j < c->dev.NBT; ++j) out.push_back(j);
+        return;
+    }
+    const int64_t r0 = (lo - P) % W;
+    for (int64_t t = 0; t < count;) {
+        const int64_t r = (r0 + t) % W;
+        out.push_back((int)((Pmax + r) / Bs));
+        t += Bs - r % Bs;
+    }
+}
+
+// Give every listed logical block of sequence b that has no physical block one from the
+// pool and write the new table entries on the stream. Nothing changes when the pool is
+// short (PSA_ERR_STATE).
+int map_blocks(psa_cache* c, int b, std::vector<int>& want, int64_t* taken, hipStream_t s,
+               psa::TableUpdate* u) {
+    int32_t* row = c->btab.data() + (size_t)b * c->dev.NBT;
+    int64_t need = 0;
+    for (int j : want)
+        if (row[j] < 0) {
+            row[j] = -2;   // counted once
+            ++need;
+        }
+    if (*taken + need > (int64_t)c->free_blk.size()) {
+        for (int j : want)
+            if (row[j] == -2) row[j] = -1;
+        return fail(PSA_ERR_STATE, "block pool exhausted: " + std::to_string(c->free_blk.size() - *taken) +
+                                       " free blocks, the call needs more");
+    }
+    for (int j : want) {
+        if (row[j] != -2) continue;
+        row[j] = c->free_blk[c->free_blk.size() - 1 - *taken];
+        *taken += 1;
+        u->idx[u->n] = b * c->dev.NBT + j;
+        u->blk[u->n] = row[j];
+        if (++u->n == psa::kTableUpdates) {
+            const hipError_t e = psa::launch_table_update(c->dev, *u, s);
+            u->n = 0;
+            if (e != hipSuccess) return hip_fail(e, "block table update");
+        }
+    }
+    return PSA_OK;
+}
+
+// Map the blocks every sequence writes when it appends n[b] tokens (all sequences or none).
+int map_append(psa_cache* c, const int32_t* n_host, int32_t n_uniform, hipStream_t s) {
+    if (c->dev.Bs == 0) return PSA_OK;
+    const int B = c->desc.max_batch;
+    // first pass: check without changing anything
+    int64_t total_new = 0;
+    std::vector<int> want;
+    for (int b = 0; b < B; ++b) {
+        const int32_t nb = n_host ? n_host[b] : n_uniform;
+        if (nb <= 0) continue;
+        want.clear();
+        blocks_of_positions(c, b, c->len[b], c->len[b] + nb, want);
+        const int32_t* row = c->btab.data() + (size_t)b * c->dev.NBT;
+        std::vector<char> seen(c->dev.NBT, 0);
+        for (int j : want)
+            if (row[j] < 0 && !seen[j]) {
+                seen[j] = 1;
+                ++total_new;
+            }
+    }
+    if (total_new > (int64_t)c->free_blk.size())
+        return fail(PSA_ERR_STATE, "block pool exhausted: " + std::to_string(c->free_blk.size()) +
+                                       " free blocks, the call needs " + std::to_string(total_new));
+    psa::TableUpdate u;
+    u.n = 0;
+    int64_t taken = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t nb = n_host ? n_host[b] : n_uniform;
+        if (nb <= 0) continue;
+        want.clear();
+        blocks_of_positions(c, b, c->len[b], c->len[b] + nb, want);
+        const int rc = map_blocks(c, b, want, &taken, s, &u);
+        if (rc != PSA_OK) return rc;
+    }
+    c->free_blk.resize(c->free_blk.size() - taken);
+    if (u.n > 0) {
+        const hipError_t e = psa::launch_table_update(c->dev, u, s);
+        if (e != hipSuccess) return hip_fail(e, "block table update");
+    }
+    return PSA_OK;
+}
+
+// Return sequence b's blocks to the pool (the device entries are cleared by the reset).
+void release_blocks(psa_cache* c, int b) {
+    if (c->dev.Bs == 0) return;
+    int32_t* row = c->btab.data() + (size_t)b * c->dev.NBT;
+    for (int j = 0; j < c->dev.NBT; ++j)
+        if (row[j] >= 0) {
+            c->free_blk.push_back(row[j]);
+            row[j] = -1;
+        }
+}
+
 }  // namespace
 
 PSA_API size_t psa_cache_bytes(const psa_cache_desc* desc) {
@@ -205,6 +336,9 @@ PSA_API int psa_cache_layout(const psa_cache_desc* desc, psa_layout* out) {
     out->total_bytes = L.total;
     out->slots = L.S;
     out->elem_bytes = L.elem;
+    out->btab_offset = L.btab;
+    out->block_size = desc->block_size;
+    out->n_blocks = L.n_blocks;
     return PSA_OK;
 }
 
@@ -250,6 +384,7 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.pool_k = base + L.pool_k;
     d.pool_v = base + L.pool_v;
     d.tags = (int32_t*)(base + L.tags);
+    d.btab = (int32_t*)(base + L.btab);
     int32_t* st = (int32_t*)(base + L.state);
     d.len[0] = st;
     d.len[1] = st + desc->max_batch;
@@ -278,6 +413,16 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.n_shared = desc->n_shared_prefixes;
     d.shared_max = desc->shared_prefix_max;
     d.pe_mode = desc->pe_mode;
+    d.Bs = desc->block_size;
+    d.bshift = 0;
+    while (d.Bs > 0 && (1 << d.bshift) < d.Bs) ++d.bshift;
+    d.NBT = d.Bs > 0 ? L.S / d.Bs : 0;
+    d.n_blocks = L.n_blocks;
+    if (d.Bs > 0) {
+        c->btab.assign((size_t)desc->max_batch * d.NBT, -1);
+        c->free_blk.reserve(L.n_blocks);
+        for (int32_t i = L.n_blocks - 1; i >= 0; --i) c->free_blk.push_back(i);
+    }
     d.scale = desc->scale > 0.f ? desc->scale : (float)(1.0 / sqrt((double)desc->head_dim));
 
     // theta_i = base^(-2i/D) in float64 on the host.
@@ -335,6 +480,7 @@ PSA_API int psa_seq_reset(psa_cache* c, int32_t seq, int32_t prefix_len, psa_str
         psa::launch_seq_reset(c->dev, seq, prefix_len, 0, -1, c->cur, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sequence reset");
     detach(c, seq);
+    release_blocks(c, seq);
     start(c, seq, prefix_len, 0);
     return PSA_OK;
 }
@@ -366,6 +512,7 @@ PSA_API int psa_seq_attach(psa_cache* c, int32_t seq, int32_t prefix_id, psa_str
         psa::launch_seq_reset(c->dev, seq, P, P, prefix_id, c->cur, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sequence attach");
     detach(c, seq);
+    release_blocks(c, seq);
     c->pid[seq] = prefix_id;
     c->attached[prefix_id] += 1;
     start(c, seq, P, P);
@@ -403,6 +550,19 @@ PSA_API int psa_seq_promote(psa_cache* c, int32_t seq, int32_t count, psa_stream
     if ((int64_t)c->npin[seq] + count > c->desc.prefix_max)
         return fail(PSA_ERR_ARG, "pinned entries would exceed prefix_max");
     if (count == 0) return PSA_OK;
+    if (c->dev.Bs > 0) {   // the prefix slots npin .. npin + count - 1 need blocks
+        std::vector<int> want;
+        for (int64_t sl = c->npin[seq]; sl < (int64_t)c->npin[seq] + count; sl = (sl / c->dev.Bs + 1) * c->dev.Bs)
+            want.push_back((int)(sl / c->dev.Bs));
+        psa::TableUpdate u;
+        u.n = 0;
+        int64_t taken = 0;
+        const int rc = map_blocks(c, seq, want, &taken, (hipStream_t)stream, &u);
+        if (rc != PSA_OK) return rc;
+        c->free_blk.resize(c->free_blk.size() - taken);
+        const hipError_t eu = psa::launch_table_update(c->dev, u, (hipStream_t)stream);
+        if (eu != hipSuccess) return hip_fail(eu, "block table update");
+    }
     const hipError_t e =
         psa::launch_promote(c->dev, seq, v.wb, count, c->npin[seq], (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "promotion");
@@ -440,6 +600,8 @@ PSA_API int psa_append(psa_cache* c, const int32_t* n_new_host, int32_t n_unifor
     if (!any) return PSA_OK;
     if (k == nullptr || v == nullptr) return fail(PSA_ERR_ARG, "k or v is NULL");
     hipStream_t s = (hipStream_t)stream;
+    const int mrc = map_append(c, n_new_host, n_uniform, s);
+    if (mrc != PSA_OK) return mrc;
     if (n_new_host != nullptr) {
         const hipError_t e = hipMemcpyAsync(c->dev.nnew, n_new_host, (size_t)B * sizeof(int32_t),
                                             hipMemcpyHostToDevice, s);
@@ -494,6 +656,8 @@ PSA_API int psa_prefill_attn(psa_cache* c, int32_t chunk, const void* q, const v
         if (c->len[b] + chunk > INT32_MAX) return fail(PSA_ERR_OVERFLOW, "sequence length overflow");
     }
     hipStream_t s = (hipStream_t)stream;
+    const int mrc = map_append(c, nullptr, chunk, s);
+    if (mrc != PSA_OK) return mrc;
     const int cur = c->cur;
     int rc = timed(c, PSA_K_PREFILL_STAGE, s, "prefill stage",
                    [&] { return psa::launch_prefill_stage(c->dev, q, k, chunk, cur, s); });
@@ -529,16 +693,27 @@ PSA_API int psa_export(psa_cache* c, int32_t seq, void* k_host, void* v_host, in
     std::vector<char> kbuf, vbuf;
     std::vector<int32_t> tags(S);
     hipError_t e = hipSuccess;
-    if (k_host) {
-        kbuf.resize(seq_bytes);
-        e = hipMemcpyAsync(kbuf.data(), (const char*)d.k + (size_t)seq * seq_bytes, seq_bytes,
-                           hipMemcpyDeviceToHost, s);
-    }
-    if (e == hipSuccess && v_host) {
-        vbuf.resize(seq_bytes);
-        e = hipMemcpyAsync(vbuf.data(), (const char*)d.v + (size_t)seq * seq_bytes, seq_bytes,
-                           hipMemcpyDeviceToHost, s);
-    }
+    // Contiguous: the sequence's [H_kv][S][D] region. Paged: the rows of each mapped block,
+    // head by head, into the same [H_kv][S][D] arrangement.
+    const bool paged = d.Bs > 0;
+    const size_t blk_rows_bytes = paged ? (size_t)d.Bs * row : 0;
+    const int32_t* brow = paged ? c->btab.data() + (size_t)seq * d.NBT : nullptr;
+    auto fetch = [&](std::vector<char>& buf, const void* dev) {
+        buf.resize(seq_bytes);
+        if (!paged)
+            return hipMemcpyAsync(buf.data(), (const char*)dev + (size_t)seq * seq_bytes, seq_bytes,
+                                  hipMemcpyDeviceToHost, s);
+        hipError_t r = hipSuccess;
+        for (int j = 0; j < d.NBT && r == hipSuccess; ++j)
+            for (size_t h = 0; h < Hkv && brow[j] >= 0 && r == hipSuccess; ++h)
+                r = hipMemcpyAsync(buf.data() + (h * S + (size_t)j * d.Bs) * row,
+                                   (const char*)dev +
+                                       psa::block_rowidx(brow[j], (int)h, 0, d.Bs, d.n_blocks) * row,
+                                   blk_rows_bytes, hipMemcpyDeviceToHost, s);
+        return r;
+    };
+    if (k_host) e = fetch(kbuf, d.k);
+    if (e == hipSuccess && v_host) e = fetch(vbuf, d.v);
     if (e == hipSuccess)
         e = hipMemcpyAsync(tags.data(), d.tags + (size_t)seq * S, S * sizeof(int32_t),
                            hipMemcpyDeviceToHost, s);
@@ -580,6 +755,19 @@ PSA_API int psa_export(psa_cache* c, int32_t seq, void* k_host, void* v_host, in
         }
     }
     *count = (int32_t)cnt;
+    return PSA_OK;
+}
+
+PSA_API int psa_seq_blocks(const psa_cache* c, int32_t seq, int32_t* table_host, int32_t* entries,
+                           int32_t* free_blocks) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (c->dev.Bs == 0) return fail(PSA_ERR_ARG, "the cache is not paged");
+    if (entries == nullptr) return fail(PSA_ERR_ARG, "entries is NULL");
+    if (!valid_seq(c, seq)) return fail(PSA_ERR_STATE, "sequence index out of range");
+    const int32_t* row = c->btab.data() + (size_t)seq * c->dev.NBT;
+    if (table_host) memcpy(table_host, row, (size_t)c->dev.NBT * sizeof(int32_t));
+    *entries = c->dev.NBT;
+    if (free_blocks) *free_blocks = (int32_t)c->free_blk.size();
     return PSA_OK;
 }
 

@@ -14,11 +14,12 @@ constexpr int kMaxGroup = 8;         // largest supported H_q / H_kv
 
 // Device view of one cache: base pointers carved out of the caller's buffer.
 struct DevCache {
-    void* k;             // [B][Hkv][S][D] storage dtype
-    void* v;             // [B][Hkv][S][D]
+    void* k;             // [B][Hkv][S][D] storage dtype, or paged [Hkv][n_blocks][Bs][D]
+    void* v;             // same layout as k
     void* pool_k;        // [n_shared][Hkv][shared_max][D] shared prefixes
     void* pool_v;
     int32_t* tags;       // [B][S]
+    int32_t* btab;       // paged: [B][NBT] physical block of each logical block, -1 if none
     int32_t* len[2];     // [B] history lengths; len[cur] is current, the other is written by append
     int32_t* pre;        // [B] prefix length P_b
     int32_t* nnew;       // [B] per-call token counts (ragged append)
@@ -34,14 +35,38 @@ struct DevCache {
     void* stage_qp;      // same, rotated at the renumbered position for prefix keys (RESET)
     // W: ring slots per (sequence, head), the largest window any sequence may use
     int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits, n_shared, shared_max, pe_mode;
+    int32_t Bs, bshift, NBT, n_blocks;   // paged: block size (0: contiguous), log2, S / Bs
     float scale;
 };
 
+// Row (kv_rowidx) and element offset (kv_row) of logical slot `slot` of (sequence b, KV
+// head h) in K or V: contiguous [B][Hkv][S][D], or paged [Hkv][n_blocks][Bs][D] through
+// the block table.
+// Paged: row of row `off` (< Bs) of physical block `blk`, KV head h. The pool is head-major
+// ([Hkv][n_blocks][Bs][D]), so a sequence's consecutive blocks are one contiguous run per
+// head, which keeps its reads as long as in the contiguous layout.
+__host__ __device__ inline size_t block_rowidx(int blk, int h, int off, int Bs, int nblk) {
+    return ((size_t)h * nblk + blk) * Bs + off;
+}
+__device__ inline size_t kv_rowidx(const DevCache& c, int b, int h, int slot) {
+    if (c.Bs == 0) return ((size_t)b * c.Hkv + h) * c.S + slot;
+    const int blk = c.btab[b * c.NBT + (slot >> c.bshift)];
+    return block_rowidx(blk, h, slot & (c.Bs - 1), c.Bs, c.n_blocks);
+}
+__device__ inline size_t kv_row(const DevCache& c, int b, int h, int slot) {
+    return kv_rowidx(c, b, h, slot) * c.D;
+}
+
+
+
 struct Layout {
-    size_t k, v, pool_k, pool_v, tags, state, inv_freq, part_o, part_ml, stage_k, stage_q, stage_qp,
-        total;
-    int32_t S, elem, max_splits;
+    size_t k, v, pool_k, pool_v, tags, btab, state, inv_freq, part_o, part_ml, stage_k, stage_q,
+        stage_qp, total;
+    int32_t S, elem, max_splits, n_blocks;
 };
+
+constexpr int kMaxBlockTable = 1024;   // paged: largest S / block_size
+constexpr int kTableUpdates = 120;     // block-table entries one update launch carries
 
 bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why);
 
@@ -72,6 +97,13 @@ __device__ inline SeqView seq_view(const DevCache& c, int b, int n) {
 
 // Kernel launchers (stream-ordered, asynchronous). They return the launch status.
 hipError_t launch_init(const DevCache& c, hipStream_t s);
+// Write n (<= kTableUpdates) block-table entries: btab[idx[i]] = blk[i].
+struct TableUpdate {
+    int32_t n;
+    int32_t idx[kTableUpdates];
+    int32_t blk[kTableUpdates];
+};
+hipError_t launch_table_update(const DevCache& c, const TableUpdate& u, hipStream_t s);
 // Start a sequence: tags -1, length `len0`, prefix length `prefix_len`, prefix entry `pid`.
 hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int len0, int pid, int cur,
                             hipStream_t s);

@@ -79,12 +79,14 @@ def kv_block(wl: Workload, starts: Sequence[int], n: int, device="cpu"
 
 
 def make_cache(wl: Workload, max_chunk: int = 0, device="cuda", n_shared: int = 0,
-               shared_max: int = 0, prefix_max: Optional[int] = None, pe: str = "continue"):
+               shared_max: int = 0, prefix_max: Optional[int] = None, pe: str = "continue",
+               block_size: int = 0, n_blocks: int = 0):
     import prefix_pinned_sliding_amd as psa
     pmax = wl.prefix_max if prefix_max is None else prefix_max
     return psa.Cache(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, pmax,
                      wl.window, wl.dtype, wl.rope_base, 0.0, max_chunk, device=device,
-                     n_shared_prefixes=n_shared, shared_prefix_max=shared_max, pe=pe)
+                     n_shared_prefixes=n_shared, shared_prefix_max=shared_max, pe=pe,
+                     block_size=block_size, n_blocks=n_blocks)
 
 
 def fill(cache, wl: Workload, n_hist: List[int], device="cuda", chunk: Optional[int] = None,

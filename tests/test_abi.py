@@ -79,10 +79,45 @@ def test_invalid_descriptions_are_rejected(psa, bad):
 
 def test_invalid_rope_base_scale_dtype(psa):
     for field, val in [("rope_base", 0.0), ("rope_base", float("inf")), ("scale", -1.0),
-                       ("dtype", 7), ("reserved", 1)]:
+                       ("dtype", 7), ("n_blocks", 1)]:
         d = good_desc(psa)
         setattr(d, field, val)
         assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0, field
+
+
+def test_paged_layout(psa):
+    # K/V become a pool of blocks [H_kv][n_blocks][Bs][D]; the block table follows the tags
+    d = good_desc(psa, prefix_max=128, block_size=64)
+    L = psa.cache_layout(d)
+    S = 128 + 4096
+    assert L.slots == S and L.block_size == 64 and L.n_blocks == 4 * S // 64
+    kv = L.n_blocks * 8 * 64 * 128 * 2
+    assert L.v_offset >= L.k_offset + kv and L.tags_offset >= L.v_offset + kv
+    assert L.btab_offset >= L.tags_offset + 4 * S * 4
+    assert L.state_offset >= L.btab_offset + 4 * (S // 64) * 4
+    for off in (L.btab_offset, L.state_offset):
+        assert off % 256 == 0
+    # a smaller pool shrinks the K/V regions only
+    small = psa.cache_layout(good_desc(psa, prefix_max=128, block_size=64, n_blocks=10))
+    assert small.n_blocks == 10
+    assert L.total_bytes - small.total_bytes == 2 * (L.n_blocks - 10) * 8 * 64 * 128 * 2
+
+
+@pytest.mark.parametrize("bad", [
+    dict(block_size=48), dict(block_size=8), dict(block_size=64),          # 100 % 64 != 0
+    dict(prefix_max=128, block_size=64, n_blocks=-1),
+    dict(prefix_max=0, window=65536, block_size=16),                      # table > 1024 entries
+    dict(n_blocks=5),                                                      # contiguous with a pool
+])
+def test_invalid_paged_descriptions(psa, bad):
+    d = good_desc(psa, **bad)
+    assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0, bad
+    assert psa.lib.psa_last_error().decode() != ""
+
+
+def test_seq_blocks_needs_a_handle(psa):
+    n = ctypes.c_int32()
+    assert psa.lib.psa_seq_blocks(None, 0, None, ctypes.byref(n), None) == psa.PSA_ERR_ARG
 
 
 def test_create_rejects_bad_buffers_before_any_device_call(psa):
