@@ -25,6 +25,12 @@ constexpr float kNeg = -1.0e30f;        // initial running max (finite: -inf - k
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kRescaleSlack = 8.0f;
 
+constexpr int kTileKeys = 64;           // keys per attention tile
+// LDS row strides (elements): K rows are read 16 bytes per lane, 8 rows per 128 bytes, so
+// a 4-bank offset between rows (D + 8) keeps them apart; V is read with transposing 8-byte
+// loads that take 4 rows x 32 bytes at once, which needs an 8-bank offset (D + 16).
+constexpr int kKPad = 8, kVPad = 16;
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
     return __builtin_bit_cast(bf16x8, w);
 }
@@ -39,35 +45,6 @@ __device__ __forceinline__ float row_sum4(float x) {
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
     return x;
-}
-
-// Column of a transposed tile for the first of 4 consecutive rows 4kq .. 4kq + 3. An
-// accumulator block pair (rows 0..15 and 16..31 of a 32-row group) gives lane group g the
-// rows 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3; storing those 8 rows side by side at
-// columns 8g .. 8g + 7 makes the matching operand one aligned 16-byte LDS read.
-__device__ __forceinline__ int vt_col(int kq) {
-    const int q = kq & 7;
-    return 32 * (kq >> 3) + (q < 4 ? 8 * q : 8 * (q - 4) + 4);
-}
-
-// Store 4 rows x 8 columns (rows 4kq .. 4kq + 3, 16-byte chunk dc of each) transposed:
-// 8 LDS rows (one per column) of 4 elements at vt_col(kq).
-template <int VSTR>
-__device__ __forceinline__ void store_transposed4(uint16_t* vt_s, int kq, int dc,
-                                                  const u32x4* r) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const uint32_t a0 = r[0][x], a1 = r[1][x], a2 = r[2][x], a3 = r[3][x];
-        u32x2 lo, hi;   // columns 2x (low halves) and 2x + 1 (high halves)
-        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        const int d0 = dc * 8 + 2 * x;
-        const int col = vt_col(kq);
-        *reinterpret_cast<u32x2*>(vt_s + d0 * VSTR + col) = lo;
-        *reinterpret_cast<u32x2*>(vt_s + (d0 + 1) * VSTR + col) = hi;
-    }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -91,6 +68,154 @@ __device__ __forceinline__ bf16x8 lds_read_tr2(const uint16_t* p0, const uint16_
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// Registers -> LDS: K and V rows as they are (consecutive lanes on consecutive 16-byte
+// chunks of a row); V^T operands are read back with transposing LDS loads.
+template <int D, int BN, int NT, int KSTR, int VSTR>
+__device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* v_s, int tid,
+                                           const u32x4* kreg, const u32x4* vreg) {
+    constexpr int CPR = D / 8;
+    constexpr int KLD = (BN * CPR) / NT;
+#pragma unroll
+    for (int rr = 0; rr < KLD; ++rr) {
+        const int ci = tid + NT * rr;
+        const int kk = ci / CPR, col = ci % CPR;
+        *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
+        *reinterpret_cast<u32x4*>(v_s + kk * VSTR + col * 8) = vreg[rr];
+    }
+}
+
+// Online-softmax state of one lane's two row blocks. m: running maximum (log2 domain),
+// kNeg until a row has seen a visible key; mb: the value the S accumulator starts from
+// (m once set, else 0), so the products arrive already shifted and exp2 needs no
+// subtraction; o: O^T accumulators; l: row sums, accumulated by an MFMA against an all-ones
+// A operand (every element of l[rb] holds the row's sum of the bf16-rounded probabilities,
+// the same values that weight V).
+template <int DB>
+struct SoftmaxRows {
+    f32x4 o[2][DB];
+    f32x4 l[2];
+    float m[2], mb[2];
+};
+
+// One 64-key tile for a wave's 32 rows: S^T = K Q^T - mb, the mask (edge tiles only), the
+// running-max update, P^T = exp2(S^T) as bf16 B operands, then O^T += V^T P^T and
+// l += 1 P^T.
+//
+// `sc` converts products to the log2 domain: 1 when the queries were staged already scaled
+// by scale * log2(e) (prefill), scale * log2(e) otherwise (training). The accumulators
+// then start at -mb / sc, and exp2 takes sc times the product.
+template <int D>
+__device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
+                                          const uint16_t* k_s, const uint16_t* v_s,
+                                          const int (&row_pos)[2], int ct0, int t1, int P, int W,
+                                          int l16, int lg, bool masked, bool mid_barrier,
+                                          float sc, float inv_sc) {
+    constexpr int KS = D / 32, DB = D / 16, KB = kTileKeys / 16, PVS = kTileKeys / 32;
+    constexpr int KSTR = D + kKPad, VSTR = D + kVPad;
+    f32x4 s[2][KB];
+    const float s0 = -st.mb[0] * inv_sc, s1 = -st.mb[1] * inv_sc;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        s[0][kb] = f32x4{s0, s0, s0, s0};
+        s[1][kb] = f32x4{s1, s1, s1, s1};
+    }
+    // k-step outer: the 8 accumulators are independent within a step, and the next step's
+    // K operands are read while this step's products run
+    bf16x8 ka[2][KB];
+    const uint16_t* kp = k_s + l16 * KSTR + 8 * lg;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        ka[0][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kb * 16 * KSTR));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                ka[(ks + 1) & 1][kb] = as_bf16x8(
+                    *reinterpret_cast<const u32x4*>(kp + kb * 16 * KSTR + (ks + 1) * 32));
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[1][ks], s[1][kb], 0, 0, 0);
+        }
+    }
+    if (mid_barrier) __syncthreads();
+    // Masked logits become -inf: exp2(-inf) is 0 for any finite shift.
+    float ml[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        if (masked) {
+            const int p = row_pos[rb];
+            int jb = ct0 + 4 * lg;
+            asm volatile("" : "+v"(jb));   // keeps the mask's arithmetic inside this branch
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = jb + kb * 16 + i;
+                    const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
+                    s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
+                }
+        }
+        ml[rb] = fmaxf(s[rb][0][0], s[rb][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = (kb == 0 ? 2 : 0); i < 4; i += 2)
+                ml[rb] = __builtin_fmaxf(__builtin_fmaxf(ml[rb], s[rb][kb][i]), s[rb][kb][i + 1]);
+    }
+    // The running max of a row only moves when some lane's own max exceeds it by the slack
+    // (or the row has none yet); test that with one ballot, do the cross-lane max only then.
+    if (__any(ml[0] * sc + st.mb[0] > st.m[0] + kRescaleSlack ||
+              ml[1] * sc + st.mb[1] > st.m[1] + kRescaleSlack)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float mt = row_max4(ml[rb]) * sc + st.mb[rb];   // absolute tile max
+            const bool need = mt > st.m[rb] + kRescaleSlack;
+            if (need) {
+                const float f = __builtin_amdgcn_exp2f(st.m[rb] - mt);
+                const float shift = (mt - st.mb[rb]) * inv_sc;
+                st.m[rb] = mt;
+                st.mb[rb] = mt;
+                st.l[rb] *= f;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) st.o[rb][db] *= f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[rb][kb] -= shift;
+            }
+        }
+    }
+    bf16x8 pb[2][PVS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ps = 0; ps < PVS; ++ps)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i] * sc);
+                pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i] * sc);
+            }
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int ps = 0; ps < PVS; ++ps) {
+        st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][ps], st.l[0], 0, 0, 0);
+        st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][ps], st.l[1], 0, 0, 0);
+    }
+    // V^T operand (d = 16 db + l16; keys in the order of P^T's accumulator layout:
+    // 32 ps + 4 lg + j, then 32 ps + 16 + 4 lg + j) by two transposing reads of V rows
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int ps = 0; ps < PVS; ++ps) {
+            const uint16_t* v0 = v_s + (32 * ps + 4 * lg + l16 / 4) * VSTR + db * 16 + 4 * (l16 % 4);
+            const bf16x8 a = lds_read_tr2(v0, v0 + 16 * VSTR);
+            st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], st.o[0][db], 0, 0, 0);
+            st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], st.o[1][db], 0, 0, 0);
+        }
 }
 
 }  // namespace

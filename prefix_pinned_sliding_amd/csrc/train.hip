@@ -6,9 +6,10 @@
 // j >= i - W + 1), rows [0, P) being the pinned prefix and later rows consecutive
 // positions. Queries and keys arrive rotated, so this is masked attention in row space.
 //
-// Forward: out and lse (natural log) per (row, query head), the prefill kernel's scheme
-// (S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, 128 rows = 128 / G
-// positions x G heads per workgroup, 64-key tiles, skipped / unmasked / masked tiles).
+// Forward: out and lse (natural log) per (row, query head), on the prefill kernel's tile
+// step and schedule (S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, 256 rows =
+// 256 / G positions x G heads per 8-wave workgroup, 64-key tiles, skipped / unmasked /
+// masked tiles, two wave groups half a tile apart, three LDS buffers).
 // Backward, three kernels:
 //   rowdot  Di = sum_d dO * O per (row, head) (float32);
 //   dkdv    one workgroup per 64-key tile; each wave keeps its 16 keys' K and V in registers
@@ -25,8 +26,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
-constexpr int kRows = 128;   // query rows per forward / dq workgroup
 constexpr int kBN = 64;      // keys per tile
+constexpr int kRows = 128;   // query rows per dq workgroup
 constexpr int kBR = 64;      // query rows per dkdv step
 
 struct TrainArgs {
@@ -103,14 +104,41 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int s32, int 
 }
 
 // ---------------------------------------------------------------------------------------
-// Forward.
+// Forward: the chunked-prefill kernel's schedule on row-space tiles. 8 waves, 256 rows per
+// workgroup in two groups of 4 waves running half a tile apart (group A passes the tile's
+// barrier after its PV products, group B after its QK^T products), three LDS buffers (tile
+// N + 1 is written into tile N - 2's), the next tile's K/V loaded into registers while the
+// current one is computed. Queries are used unscaled; tile_step applies scale * log2(e) to
+// the products in float32.
+constexpr int kFwdWaves = 8;
+constexpr int kFwdBlock = 64 * kFwdWaves;
+constexpr int kFwdRows = 32 * kFwdWaves;
+
+// This thread's share of key rows t0 .. t0 + 63 (rows past `last` repeat row `last`) of
+// K and V into registers, in stage_tile's order.
+template <int D>
+__device__ __forceinline__ void fetch_rows(const TrainArgs& a, size_t kv0, int t0, int last,
+                                           int tid, u32x4* kreg, u32x4* vreg) {
+    constexpr int CPR = D / 8;
+    constexpr int KLD = (kTileKeys * CPR) / kFwdBlock;
+#pragma unroll
+    for (int rr = 0; rr < KLD; ++rr) {
+        const int ci = tid + kFwdBlock * rr;
+        const int kk = min(ci / CPR, last), col = ci % CPR;
+        const size_t off = (kv0 + (size_t)(t0 + kk) * a.Hkv) * D + col * 8;
+        kreg[rr] = *reinterpret_cast<const u32x4*>(a.k + off);
+        vreg[rr] = *reinterpret_cast<const u32x4*>(a.v + off);
+    }
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n_qtiles) {
-    constexpr int BQ = kRows / G;
-    constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    constexpr int KSTR = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
+__global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, int n_qtiles) {
+    constexpr int BQ = kFwdRows / G;
+    constexpr int KS = D / 32, DB = D / 16;
+    constexpr int KSTR = D + kKPad, VSTR = D + kVPad;
+    constexpr int KLD = (kTileKeys * (D / 8)) / kFwdBlock;
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[3][kTileKeys * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t v_s[3][kTileKeys * VSTR];
 
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
@@ -124,7 +152,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const float sc = a.scale * kLog2e;
+    const float sc = a.scale * kLog2e, inv_sc = 1.f / sc;
 
     int row_pos[2];
     bf16x8 qop[2][KS];
@@ -138,105 +166,58 @@ __global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n
         for (int ks = 0; ks < KS; ++ks)
             qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.q + off + ks * 32));
     }
-    f32x4 o[2][DB];
-    float m[2] = {kNeg, kNeg}, lp[2] = {0.f, 0.f};
+    SoftmaxRows<DB> st;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+        st.m[rb] = kNeg;
+        st.mb[rb] = 0.f;
+        st.l[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) st.o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const KeyWalk wk{min(P, p_hi + 1), max(P, p_lo - W + 1), p_hi + 1};
     const size_t kv0 = (size_t)b * a.T * a.Hkv + h;   // row j at (kv0 + j * Hkv) * D
-    int seg = 0, t0 = -kBN;
+    auto seg_hi = [&](int sg) { return sg == 0 ? wk.hi0 : wk.hi1; };
+    // every wave runs the same walk, so all pass the same number of barriers
+    const bool grp_b = __builtin_amdgcn_readfirstlane(wave) >= kFwdWaves / 2;
+    u32x4 kreg[KLD], vreg[KLD];
+    int seg = 0, t0 = -kTileKeys;
+    if (wk.next(seg, t0)) {
+        int ct0 = t0, chi = seg_hi(seg), cur = 0;
+        fetch_rows<D>(a, kv0, t0, min(t0 + kTileKeys, chi) - 1 - t0, tid, kreg, vreg);
+        stage_tile<D, kTileKeys, kFwdBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
+        bool have = wk.next(seg, t0);
+        if (have) fetch_rows<D>(a, kv0, t0, min(t0 + kTileKeys, seg_hi(seg)) - 1 - t0, tid, kreg, vreg);
+        __syncthreads();
 #pragma unroll 1
-    while (wk.next(seg, t0)) {
-        const int t1 = min(t0 + kBN, seg == 0 ? wk.hi0 : wk.hi1);
-        const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) && (t1 - 1 < P || t0 >= p_hi - W + 1);
-        __syncthreads();
-        {
-            auto off = [&](int r) { return (kv0 + (size_t)(t0 + r) * a.Hkv) * D; };
-            RowTile<D, kBN> kr, vr;
-            kr.load(a.k, tid, t1 - 1 - t0, off);
-            vr.load(a.v, tid, t1 - 1 - t0, off);
-            kr.template store<KSTR>(k_s, tid);
-            vr.template store<KSTR>(v_s, tid);
-        }
-        __syncthreads();
-
-        f32x4 s[2][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            s[0][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[1][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ka = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(k_s + (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg));
-                s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[0][ks], s[0][kb], 0, 0, 0);
-                s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[1][ks], s[1][kb], 0, 0, 0);
+        while (true) {
+            const int nt0 = t0, nhi = seg_hi(seg);
+            const int nxt = cur == 2 ? 0 : cur + 1;
+            bool have_next = false;
+            if (have) {
+                stage_tile<D, kTileKeys, kFwdBlock, KSTR, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
+                have_next = wk.next(seg, t0);
+                if (have_next)
+                    fetch_rows<D>(a, kv0, t0, min(t0 + kTileKeys, seg_hi(seg)) - 1 - t0, tid, kreg, vreg);
             }
+            const int t1 = min(ct0 + kTileKeys, chi);
+            const bool full = (ct0 + kTileKeys == t1) && (t1 - 1 <= p_lo) &&
+                              (t1 - 1 < P || ct0 >= p_hi - W + 1);
+            tile_step<D>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, t1, P, W, l16, lg, !full, grp_b,
+                         sc, inv_sc);
+            if (!grp_b) __syncthreads();
+            if (!have) break;
+            ct0 = nt0;
+            chi = nhi;
+            have = have_next;
+            cur = nxt;
         }
-        float ml[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = t0 + kb * 16 + 4 * lg + i;
-                    const float x = s[rb][kb][i] * sc;
-                    s[rb][kb][i] = (full || (j < t1 && visible(row_pos[rb], j, P, W))) ? x : -INFINITY;
-                }
-            ml[rb] = s[rb][0][0];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ml[rb] = fmaxf(ml[rb], s[rb][kb][i]);
-        }
-        if (__any(ml[0] > m[0] + kRescaleSlack || ml[1] > m[1] + kRescaleSlack)) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const float mt = row_max4(ml[rb]);
-                const bool need = mt > m[rb] + kRescaleSlack;
-                const float f = need ? __builtin_amdgcn_exp2f(m[rb] - mt) : 1.f;
-                m[rb] = need ? mt : m[rb];
-                lp[rb] *= f;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) o[rb][db] *= f;
-            }
-        }
-        bf16x8 pb[2][PVS];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            float acc = 0.f;
-#pragma unroll
-            for (int ps = 0; ps < PVS; ++ps) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i] - m[rb]);
-                    pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i] - m[rb]);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    bf16x2 two = {pb[rb][ps][i], pb[rb][ps][i + 1]};
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, acc, false);
-                }
-            }
-            lp[rb] += acc;
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int ps = 0; ps < PVS; ++ps) {
-                const bf16x8 va = tr_operand<KSTR>(v_s, ps, db * 16, l16, lg);
-                o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][ps], o[0][db], 0, 0, 0);
-                o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][ps], o[1][db], 0, 0, 0);
-            }
     }
 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const float l = row_sum4(lp[rb]);
+        const float l = st.l[rb][0];
         const int r = 32 * wave + 16 * rb + l16;
         if (row_pos[rb] >= len) continue;
         const size_t row = ((size_t)b * a.T + row_pos[rb]) * a.Hq + h * G + r % G;
@@ -244,11 +225,11 @@ __global__ __launch_bounds__(kBlock, 2) void train_fwd_kernel(TrainArgs a, int n
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             u32x2 w;
-            w[0] = pack_bf16(o[rb][db][0] * inv, o[rb][db][1] * inv);
-            w[1] = pack_bf16(o[rb][db][2] * inv, o[rb][db][3] * inv);
+            w[0] = pack_bf16(st.o[rb][db][0] * inv, st.o[rb][db][1] * inv);
+            w[1] = pack_bf16(st.o[rb][db][2] * inv, st.o[rb][db][3] * inv);
             *reinterpret_cast<u32x2*>(a.out + row * D + db * 16 + 4 * lg) = w;
         }
-        if (lg == 0) a.lse[row] = (m[rb] + __log2f(l)) * kLn2;
+        if (lg == 0) a.lse[row] = (st.m[rb] + __log2f(l)) * kLn2;
     }
 }
 
@@ -536,14 +517,18 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
 
 template <int D, int G>
 hipError_t launch_train_g(const TrainArgs& a, bool backward, hipStream_t s) {
+    if (!backward) {
+        constexpr int BF = kFwdRows / G;
+        const int f_tiles = (a.T + BF - 1) / BF;
+        const int f_total = f_tiles * a.Hkv * a.B;
+        hipLaunchKernelGGL((train_fwd_kernel<D, G>), dim3(((f_total + 7) / 8) * 8), dim3(kFwdBlock),
+                           0, s, a, f_tiles);
+        return hipGetLastError();
+    }
     constexpr int BQ = kRows / G;
     const int n_qtiles = (a.T + BQ - 1) / BQ;
     const int q_total = n_qtiles * a.Hkv * a.B;
     const int q_grid = ((q_total + 7) / 8) * 8;
-    if (!backward) {
-        hipLaunchKernelGGL((train_fwd_kernel<D, G>), dim3(q_grid), dim3(kBlock), 0, s, a, n_qtiles);
-        return hipGetLastError();
-    }
     const size_t rows = (size_t)a.B * a.T * a.Hq;
     hipLaunchKernelGGL((train_rowdot_kernel<D>), dim3((unsigned)((rows + kBlock - 1) / kBlock)),
                        dim3(kBlock), 0, s, a);
