@@ -170,22 +170,29 @@ int64_t visible_count(const psa_cache* c, int b) {
     return (int64_t)v.n_pre + v.n_win;
 }
 
-// Automatic split length. Split the longest sequence into ns pieces with ns chosen so the
-// grid is about two rounds of the workgroups that fit on the device at once (measured:
-// longer splits amortise each workgroup's set-up and final reduction, and whole rounds
-// avoid a ragged tail); the pieces are equal so no split is a short remainder. Never
-// shorter than kSplitGranule entries.
+// Automatic split length. Cut a sequence of `ref` visible entries into ns pieces with ns
+// chosen so the grid is about two rounds of the workgroups that fit on the device at once
+// (measured: longer splits amortise each workgroup's set-up and final reduction, and
+// whole rounds avoid a ragged tail). ref is the longest sequence when there are at least
+// as many (sequence, KV head) pairs as resident workgroups: then every pair is one piece
+// and splitting long sequences would only add uneven pieces. With fewer pairs the batch
+// must be split for parallelism, and ref is the mean length, so that the pieces of a
+// ragged batch add up to about two rounds instead of leaving short sequences' workgroups
+// underfilled. Never shorter than kSplitGranule entries.
 int auto_split_tokens(psa_cache* c) {
-    int64_t longest = 1;
+    int64_t longest = 1, sum = 0;
     for (int b = 0; b < c->desc.max_batch; ++b) {
         const int64_t t = visible_count(c, b);
+        sum += t;
         if (t > longest) longest = t;
     }
     if (c->resident_wgs == 0) c->resident_wgs = psa::decode_resident_wgs(c->dev);
     const int64_t pairs = (int64_t)c->desc.max_batch * c->desc.n_kv_heads;
+    const int64_t mean = (sum + c->desc.max_batch - 1) / c->desc.max_batch;
+    const int64_t ref = pairs < c->resident_wgs && mean > 0 ? mean : longest;
     int64_t ns = (2 * (int64_t)c->resident_wgs) / pairs;
     if (ns < 1) ns = 1;
-    int64_t L = (longest + ns - 1) / ns;
+    int64_t L = (ref + ns - 1) / ns;
     if (L < psa::kSplitGranule) L = psa::kSplitGranule;
     return (int)L;
 }
