@@ -72,6 +72,22 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
     r /= groups;
     const int j = (int)(r % chunk);
     const int b = (int)(r / chunk);
+    const size_t tok = (size_t)b * chunk + j;
+    const int h0 = grp * kStageHeads;
+    // Every input element of the group is loaded before anything is stored: the staging
+    // buffers could alias the inputs as far as the compiler knows, so loads issued after a
+    // store would each wait for it. A group past the last head repeats it and stores nothing.
+    double xs[kStageHeads], ys[kStageHeads];
+    size_t offs[kStageHeads];
+#pragma unroll
+    for (int t = 0; t < kStageHeads; ++t) {
+        const int hh = min(h0 + t, heads - 1);
+        const bool is_key = hh < c.Hkv;
+        offs[t] = is_key ? (tok * c.Hkv + hh) * D : (tok * c.Hq + (hh - c.Hkv)) * D;
+        const uint16_t* src = is_key ? k : q;
+        xs[t] = bf16_bits_to_f64(src[offs[t] + i]);
+        ys[t] = bf16_bits_to_f64(src[offs[t] + i + H]);
+    }
     const int p = len_cur[b] + j;
     double sn, cs;
     angle_sincos(p, c.inv_freq[i], &sn, &cs);
@@ -85,17 +101,15 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
         const int pp = p < P ? p : P + min(c.wlen[b], p + 1 - c.wfloor[b]) - 1;
         if (pp != p) angle_sincos(pp, c.inv_freq[i], &snp, &csp);
     }
-    const size_t tok = (size_t)b * chunk + j;
     const double sc = (double)c.scale * (double)kLog2e;
-    const int h_end = min(heads, (grp + 1) * kStageHeads);
 #pragma unroll
-    for (int hh = grp * kStageHeads; hh < h_end; ++hh) {
-        const bool is_key = hh < c.Hkv;
-        const size_t off = is_key ? (tok * c.Hkv + hh) * D : (tok * c.Hq + (hh - c.Hkv)) * D;
-        const uint16_t* src = is_key ? k : q;
+    for (int t = 0; t < kStageHeads; ++t) {
+        const int hh = h0 + t;
+        if (hh >= heads) break;
+        const size_t off = offs[t];
         double xr, yr;
-        rotate_with(bf16_bits_to_f64(src[off + i]), bf16_bits_to_f64(src[off + i + H]), sn, cs, &xr, &yr);
-        if (is_key) {
+        rotate_with(xs[t], ys[t], sn, cs, &xr, &yr);
+        if (hh < c.Hkv) {
             uint16_t* ko = (uint16_t*)c.stage_k;
             ko[off + i] = f64_to_bf16_bits(xr);
             ko[off + i + H] = f64_to_bf16_bits(yr);
@@ -105,8 +119,7 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
             qo[off + i + H] = q_to_bf16(yr * sc);
             if (reset) {
                 double xp, yp;
-                rotate_with(bf16_bits_to_f64(src[off + i]), bf16_bits_to_f64(src[off + i + H]),
-                            snp, csp, &xp, &yp);
+                rotate_with(xs[t], ys[t], snp, csp, &xp, &yp);
                 uint16_t* qp = (uint16_t*)c.stage_qp;
                 qp[off + i] = q_to_bf16(xp * sc);
                 qp[off + i + H] = q_to_bf16(yp * sc);
