@@ -155,11 +155,17 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
     const int j = (int)(r % n_stride);
     const int b = (int)(r / n_stride);
 
+    // Inputs first (rows j < n_stride are always in the tensor): a store (length, tag, K)
+    // could alias them as far as the compiler knows, so a load issued after one would wait
+    // for it.
+    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * D;
+    const T kx = k[src + i], ky = k[src + i + H];
+    const T vx = v[src + i], vy = v[src + i + H];
+    const double theta = c.inv_freq[i];
     const int nb = ragged ? c.nnew[b] : n_uniform;
     const int L0 = len_cur[b];
     if (j == 0 && h == 0 && i == 0) len_next[b] = L0 + nb;
     if (j >= nb) return;
-
     const int p = L0 + j;
     const int P = c.pre[b];
     const int wf = c.wfloor[b], wl = c.wlen[b];
@@ -180,22 +186,21 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
         if (p < wb1) return;                         // dropped within this call
         slot = c.Pmax + (p - P) % c.W;
     }
-    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * D;
     const size_t dst = kv_rowidx(c, b, h, slot) * D;
     T* K = (T*)c.k;
     T* V = (T*)c.v;
     if (k_rotated) {
-        K[dst + i] = k[src + i];
-        K[dst + i + H] = k[src + i + H];
+        K[dst + i] = kx;
+        K[dst + i + H] = ky;
     } else {
         double sn, cs, xr, yr;
-        angle_sincos(p, c.inv_freq[i], &sn, &cs);
-        rotate_with(to_f64(k[src + i]), to_f64(k[src + i + H]), sn, cs, &xr, &yr);
+        angle_sincos(p, theta, &sn, &cs);
+        rotate_with(to_f64(kx), to_f64(ky), sn, cs, &xr, &yr);
         K[dst + i] = store_as(xr, (T*)nullptr);
         K[dst + i + H] = store_as(yr, (T*)nullptr);
     }
-    V[dst + i] = v[src + i];
-    V[dst + i + H] = v[src + i + H];
+    V[dst + i] = vx;
+    V[dst + i + H] = vy;
     if (h == 0 && i == 0) c.tags[(size_t)b * c.S + slot] = p;
 }
 
@@ -219,6 +224,9 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(DevCache c, const uint32
     const int j = (int)(r % n_stride);
     const int b = (int)(r / n_stride);
     const int nb = n_stride;
+    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * CPR + ch;
+    const u32x4 kk = reinterpret_cast<const u32x4*>(k)[src];   // before any store (see above)
+    const u32x4 vv = reinterpret_cast<const u32x4*>(v)[src];
     const int L0 = len_cur[b];
     if (j == 0 && h == 0 && ch == 0) len_next[b] = L0 + nb;
     const int p = L0 + j;
@@ -241,10 +249,9 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(DevCache c, const uint32
         if (p < wb1) return;
         slot = c.Pmax + (p - P) % c.W;
     }
-    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * CPR + ch;
     const size_t dst = kv_rowidx(c, b, h, slot) * CPR + ch;
-    reinterpret_cast<u32x4*>(c.k)[dst] = reinterpret_cast<const u32x4*>(k)[src];
-    reinterpret_cast<u32x4*>(c.v)[dst] = reinterpret_cast<const u32x4*>(v)[src];
+    reinterpret_cast<u32x4*>(c.k)[dst] = kk;
+    reinterpret_cast<u32x4*>(c.v)[dst] = vv;
     if (h == 0 && ch == 0) c.tags[(size_t)b * c.S + slot] = p;
 }
 
