@@ -284,3 +284,41 @@ def test_paged_decode_full_size():
     check_blocks(caches[1], wl.batch)
     for s in (0, 37):
         np.testing.assert_array_equal(bits(caches[0].export(s)[0]), bits(caches[1].export(s)[0]))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [(32, 8, 128, torch.bfloat16), (64, 8, 128, torch.bfloat16),
+                                            (16, 4, 64, torch.bfloat16), (8, 8, 64, torch.float32)])
+def test_paged_decode_and_prefill_head_layouts(Hq, Hkv, D, dtype):
+    # Every query-group size (G = 1, 4, 8) and head dimension has its own decode (and, for
+    # bf16, prefill) instantiation; each must give the contiguous cache's exact results.
+    W, Pmax, Bs = 256, 64, 32
+    prefix = [30, 0, 64]
+    n = [400, 100, 700]
+    B = len(prefix)
+    C = 48 if dtype == torch.bfloat16 else 0
+    wl = configs.Workload("pgh", dtype, B, Hq, Hkv, D, W, prefix, [1] * B, "decode")
+    caches = [drive.make_cache(wl, prefix_max=Pmax, max_chunk=C),
+              drive.make_cache(wl, prefix_max=Pmax, max_chunk=C, block_size=Bs)]
+    for c in caches:
+        drive.fill(c, wl, n)
+    if C:
+        q = drive.query_block(wl, n, C, "cuda")
+        k, v = drive.kv_block(wl, n, C, "cuda")
+        o0, o1 = (c.prefill(q, k, v) for c in caches)
+        assert torch.equal(o0, o1)
+        n = [x + C for x in n]
+    k, v = drive.kv_block(wl, n, 1, "cuda")
+    q = drive.queries(wl, n, "cuda")
+    outs = []
+    for c in caches:
+        c.append(k, v)
+        outs.append(c.decode(q))
+    assert torch.equal(outs[0], outs[1])
+    same_export(caches[0], caches[1], B)
+    check_blocks(caches[1], B)
+    out = outs[1].double().cpu().numpy()
+    qc = q.double().cpu().numpy()
+    for s in range(B):
+        ref, _ = attn.decode_query(qc[s], n[s], drive.hist_provider(wl, s), prefix[s], W, Hkv,
+                                   wl.rope_base, wl.scale)
+        tol_check(out[s], ref, dtype, f"seq {s}")
