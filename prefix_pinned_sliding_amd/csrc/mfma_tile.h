@@ -99,22 +99,19 @@ struct SoftmaxRows {
     float m[2], mb[2];
 };
 
-// One 64-key tile for a wave's 32 rows: S^T = K Q^T - mb, the mask (edge tiles only), the
-// running-max update, P^T = exp2(S^T) as bf16 B operands, then O^T += V^T P^T and
-// l += 1 P^T.
+// The three phases of one 64-key tile for a wave's 32 rows. tile_qk: S^T = K Q^T - mb.
+// tile_softmax: the mask (edge tiles only), the running-max update (rescaling O and l when
+// it moves), P^T = exp2(S^T) as bf16 B operands. tile_pv: l += 1 P^T and O^T += V^T P^T.
 //
 // `sc` converts products to the log2 domain: 1 when the queries were staged already scaled
 // by scale * log2(e) (prefill), scale * log2(e) otherwise (training). The accumulators
 // then start at -mb / sc, and exp2 takes sc times the product.
 template <int D>
-__device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
-                                          const uint16_t* k_s, const uint16_t* v_s,
-                                          const int (&row_pos)[2], int ct0, int t1, int P, int W,
-                                          int l16, int lg, bool masked, bool mid_barrier,
-                                          float sc, float inv_sc) {
-    constexpr int KS = D / 32, DB = D / 16, KB = kTileKeys / 16, PVS = kTileKeys / 32;
-    constexpr int KSTR = D + kKPad, VSTR = D + kVPad;
-    f32x4 s[2][KB];
+__device__ __forceinline__ void tile_qk(f32x4 (&s)[2][kTileKeys / 16], const SoftmaxRows<D / 16>& st,
+                                        const bf16x8 (&qop)[2][D / 32], const uint16_t* k_s,
+                                        int l16, int lg, float inv_sc) {
+    constexpr int KS = D / 32, KB = kTileKeys / 16;
+    constexpr int KSTR = D + kKPad;
     const float s0 = -st.mb[0] * inv_sc, s1 = -st.mb[1] * inv_sc;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -142,7 +139,14 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
             s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[1][ks], s[1][kb], 0, 0, 0);
         }
     }
-    if (mid_barrier) __syncthreads();
+}
+
+template <int D>
+__device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][kTileKeys / 32], f32x4 (&s)[2][kTileKeys / 16],
+                                             SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
+                                             int ct0, int t1, int P, int W, int lg, bool masked,
+                                             float sc, float inv_sc) {
+    constexpr int DB = D / 16, KB = kTileKeys / 16, PVS = kTileKeys / 32;
     // Masked logits become -inf: exp2(-inf) is 0 for any finite shift.
     float ml[2];
 #pragma unroll
@@ -188,7 +192,6 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
             }
         }
     }
-    bf16x8 pb[2][PVS];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -198,6 +201,13 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
                 pb[rb][ps][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps][i] * sc);
                 pb[rb][ps][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * ps + 1][i] * sc);
             }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv(SoftmaxRows<D / 16>& st, const bf16x8 (&pb)[2][kTileKeys / 32],
+                                        const uint16_t* v_s, int l16, int lg) {
+    constexpr int DB = D / 16, PVS = kTileKeys / 32;
+    constexpr int VSTR = D + kVPad;
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 #pragma unroll
@@ -216,6 +226,22 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
             st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][ps], st.o[0][db], 0, 0, 0);
             st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][ps], st.o[1][db], 0, 0, 0);
         }
+}
+
+// One whole tile: the three phases in order, with an optional workgroup barrier between
+// the products S^T and the softmax.
+template <int D>
+__device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
+                                          const uint16_t* k_s, const uint16_t* v_s,
+                                          const int (&row_pos)[2], int ct0, int t1, int P, int W,
+                                          int l16, int lg, bool masked, bool mid_barrier,
+                                          float sc, float inv_sc) {
+    f32x4 s[2][kTileKeys / 16];
+    tile_qk<D>(s, st, qop, k_s, l16, lg, inv_sc);
+    if (mid_barrier) __syncthreads();
+    bf16x8 pb[2][kTileKeys / 32];
+    tile_softmax<D>(pb, s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
+    tile_pv<D>(st, pb, v_s, l16, lg);
 }
 
 }  // namespace
