@@ -142,17 +142,30 @@ int hip_fail(hipError_t e, const char* what) {
 template <typename F>
 int timed(psa_cache* c, int kernel, hipStream_t s, const char* what, F&& launch) {
     EventPair ev{kernel, nullptr, nullptr};
+    auto drop = [&] {   // events of a launch that will not be read
+        if (ev.start) hipEventDestroy(ev.start);
+        if (ev.stop) hipEventDestroy(ev.stop);
+    };
     if (c->profiling) {
         hipError_t e = hipEventCreate(&ev.start);
         if (e == hipSuccess) e = hipEventCreate(&ev.stop);
         if (e == hipSuccess) e = hipEventRecord(ev.start, s);
-        if (e != hipSuccess) return hip_fail(e, "profiling event");
+        if (e != hipSuccess) {
+            drop();
+            return hip_fail(e, "profiling event");
+        }
     }
     const hipError_t e = launch();
-    if (e != hipSuccess) return hip_fail(e, what);
+    if (e != hipSuccess) {
+        drop();
+        return hip_fail(e, what);
+    }
     if (c->profiling) {
         const hipError_t e2 = hipEventRecord(ev.stop, s);
-        if (e2 != hipSuccess) return hip_fail(e2, "profiling event");
+        if (e2 != hipSuccess) {
+            drop();
+            return hip_fail(e2, "profiling event");
+        }
         c->pending.push_back(ev);
     }
     return PSA_OK;
