@@ -19,6 +19,7 @@
 // more than 2^8), and partial sums are combined across lane groups and waves once per
 // split. K3 then merges the splits of each (sequence, query head).
 #include "psa_internal.h"
+#include "rope_round.h"
 
 namespace psa {
 namespace {
@@ -105,20 +106,6 @@ __device__ __forceinline__ float row_group_sum(float x) {
 #ifndef PSA_DECODE_PIPELINE
 #define PSA_DECODE_PIPELINE 1    // 1: load the next iteration's K/V before computing this one
 #endif
-
-// Rotated, scaled query pair for position p (fp32 result). The angle p * theta_i is formed
-// and reduced modulo 2*pi in float64, then sin/cos are taken in float32: queries are never
-// stored, so float32 accuracy (~1e-7 relative) is all the logits need.
-__device__ __forceinline__ void rotate_query(float x, float y, int p, double theta, float sc,
-                                             float* xr, float* yr) {
-    const double phi = (double)p * theta;
-    const double two_pi = 6.283185307179586;
-    const double r = phi - two_pi * rint(phi * (1.0 / two_pi));
-    float sn, cs;
-    sincosf((float)r, &sn, &cs);
-    *xr = (x * cs - y * sn) * sc;
-    *yr = (x * sn + y * cs) * sc;
-}
 
 template <int DT, int D, int LPK, int U>
 struct KVTile {

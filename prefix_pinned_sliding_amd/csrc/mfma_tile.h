@@ -103,7 +103,7 @@ struct SoftmaxRows {
 // tile_softmax: the mask (edge tiles only), the running-max update (rescaling O and l when
 // it moves), P^T = exp2(S^T) as bf16 B operands. tile_pv: l += 1 P^T and O^T += V^T P^T.
 //
-// `sc` converts products to the log2 domain: 1 when the queries were staged already scaled
+// `sc` converts products to the log2 domain: 1 when the queries were loaded already scaled
 // by scale * log2(e) (prefill), scale * log2(e) otherwise (training). The accumulators
 // then start at -mb / sc, and exp2 takes sc times the product.
 template <int D>

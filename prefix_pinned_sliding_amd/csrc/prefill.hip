@@ -1,5 +1,4 @@
-// Chunked-prefill attention on MFMA (K4) and the staging of a chunk's rotated queries and
-// keys.
+// Chunked-prefill attention on MFMA (K4) and the staging of a chunk's rotated keys.
 //
 // A chunk of C new tokens at positions n .. n + C - 1 of a sequence: query row c (at
 // p = n + c) attends to A(p) ([PS] 03): the pinned prefix, the window [p - w + 1, p] and
@@ -22,8 +21,9 @@
 // keys, which is exactly the B-operand layout P^T needs, so probabilities never leave
 // registers; row maxima need one cross-lane exchange per tile, row sums come from an MFMA
 // against ones. K and V are staged row-major; V^T operands are read with transposing LDS
-// loads. Softmax runs on exp2 with the scale folded into the staged queries; the running
-// max is raised only when a tile exceeds it by more than 2^8.
+// loads. Softmax runs on exp2 with the scale folded into the queries (rotated and scaled
+// as each workgroup loads them); the running max is raised only when a tile exceeds it by
+// more than 2^8.
 //
 // Schedule: the waves form two groups of four, one wave of each on every SIMD. Group A
 // passes the tile's barrier after its PV products, group B right after its QK^T products,
@@ -47,21 +47,18 @@ constexpr int kRows = 32 * kPfWaves;     // rows (position x head) per workgroup
 constexpr int kBN = kTileKeys;           // keys per tile
 constexpr int kNBuf = 3;                 // LDS tile buffers
 
-// float64 -> bfloat16 for staged queries: the same single rounding as stored keys.
-__device__ __forceinline__ uint16_t q_to_bf16(double x) { return f64_to_bf16_bits(x); }
-
-// Stage a chunk: keys rotated at their absolute positions and rounded once (the bytes the
-// cache will hold), queries rotated, multiplied by scale * log2(e) and rounded to bf16.
-// One thread per (sequence, token, group of kStageHeads heads, pair): the angle's sin/cos
-// is computed once per group; heads [0, Hkv) are keys, [Hkv, Hkv + Hq) queries.
+// Stage a chunk's keys: rotated at their absolute positions and rounded once (the bytes the
+// cache will hold). One thread per (sequence, token, group of kStageHeads KV heads, pair):
+// the angle's sin/cos is computed once per group. (Queries are rotated by the attention
+// kernel as it loads them.)
 constexpr int kStageHeads = 4;
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const uint16_t* q,
-                                                             const uint16_t* k, int chunk,
+__global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const uint16_t* k,
+                                                             int chunk,
                                                              const int32_t* __restrict__ len_cur) {
     constexpr int H = D / 2;
-    const int heads = c.Hkv + c.Hq;
+    const int heads = c.Hkv;
     const int groups = (heads + kStageHeads - 1) / kStageHeads;
     const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
     const size_t total = (size_t)c.B * chunk * groups * H;
@@ -75,59 +72,55 @@ __global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const u
     const size_t tok = (size_t)b * chunk + j;
     const int h0 = grp * kStageHeads;
     // Every input element of the group is loaded before anything is stored: the staging
-    // buffers could alias the inputs as far as the compiler knows, so loads issued after a
+    // buffer could alias the input as far as the compiler knows, so loads issued after a
     // store would each wait for it. A group past the last head repeats it and stores nothing.
     double xs[kStageHeads], ys[kStageHeads];
     size_t offs[kStageHeads];
 #pragma unroll
     for (int t = 0; t < kStageHeads; ++t) {
         const int hh = min(h0 + t, heads - 1);
-        const bool is_key = hh < c.Hkv;
-        offs[t] = is_key ? (tok * c.Hkv + hh) * D : (tok * c.Hq + (hh - c.Hkv)) * D;
-        const uint16_t* src = is_key ? k : q;
-        xs[t] = bf16_bits_to_f64(src[offs[t] + i]);
-        ys[t] = bf16_bits_to_f64(src[offs[t] + i + H]);
+        offs[t] = (tok * c.Hkv + hh) * D;
+        xs[t] = bf16_bits_to_f64(k[offs[t] + i]);
+        ys[t] = bf16_bits_to_f64(k[offs[t] + i + H]);
     }
     const int p = len_cur[b] + j;
     double sn, cs;
     angle_sincos(p, c.inv_freq[i], &sn, &cs);
-    // RESET: for prefix keys the query sits at its renumbered position, its index in the
-    // list [prefix, window] after it is appended: p inside the prefix, else
-    // P + min(w_b, p + 1 - wfloor) - 1
-    const bool reset = c.pe_mode == PSA_PE_RESET;
-    double snp = sn, csp = cs;
-    if (reset) {
-        const int P = c.pre[b];
-        const int pp = p < P ? p : P + min(c.wlen[b], p + 1 - c.wfloor[b]) - 1;
-        if (pp != p) angle_sincos(pp, c.inv_freq[i], &snp, &csp);
-    }
-    const double sc = (double)c.scale * (double)kLog2e;
+    uint16_t* ko = (uint16_t*)c.stage_k;
 #pragma unroll
     for (int t = 0; t < kStageHeads; ++t) {
-        const int hh = h0 + t;
-        if (hh >= heads) break;
-        const size_t off = offs[t];
+        if (h0 + t >= heads) break;
         double xr, yr;
         rotate_with(xs[t], ys[t], sn, cs, &xr, &yr);
-        if (hh < c.Hkv) {
-            uint16_t* ko = (uint16_t*)c.stage_k;
-            ko[off + i] = f64_to_bf16_bits(xr);
-            ko[off + i + H] = f64_to_bf16_bits(yr);
-        } else {
-            uint16_t* qo = (uint16_t*)c.stage_q;
-            qo[off + i] = q_to_bf16(xr * sc);
-            qo[off + i + H] = q_to_bf16(yr * sc);
-            if (reset) {
-                double xp, yp;
-                rotate_with(xs[t], ys[t], snp, csp, &xp, &yp);
-                uint16_t* qp = (uint16_t*)c.stage_qp;
-                qp[off + i] = q_to_bf16(xp * sc);
-                qp[off + i + H] = q_to_bf16(yp * sc);
-            }
-        }
+        ko[offs[t] + i] = f64_to_bf16_bits(xr);
+        ko[offs[t] + i + H] = f64_to_bf16_bits(yr);
     }
 }
 
+// MFMA B operands of one 16-row block from a query row of the chunk: this lane's dims
+// 32 ks + 8 lg + j, rotated at position p (dim i < D / 2 pairs with i + D / 2, which the same
+// lane holds in k-step ks + KS / 2), multiplied by `sc` and rounded to bf16. `qrow` points
+// at the row's element 8 lg.
+template <int D>
+__device__ __forceinline__ void load_query(bf16x8 (&qo)[D / 32], const uint16_t* qrow, int p,
+                                           const double* inv_freq, int lg, float sc) {
+    constexpr int KS = D / 32, HS = KS / 2;
+#pragma unroll
+    for (int ks = 0; ks < HS; ++ks) {
+        const u32x4 xw = *reinterpret_cast<const u32x4*>(qrow + ks * 32);
+        const u32x4 yw = *reinterpret_cast<const u32x4*>(qrow + (ks + HS) * 32);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t xb = (j & 1) ? (xw[j / 2] & 0xFFFF0000u) : (xw[j / 2] << 16);
+            const uint32_t yb = (j & 1) ? (yw[j / 2] & 0xFFFF0000u) : (yw[j / 2] << 16);
+            float xr, yr;
+            rotate_query_bf16(__uint_as_float(xb), __uint_as_float(yb), p, inv_freq[ks * 32 + 8 * lg + j],
+                              sc, &xr, &yr);
+            qo[ks][j] = (__bf16)xr;
+            qo[ks + HS][j] = (__bf16)yr;
+        }
+    }
+}
 
 // The key ranges of a workgroup, in walk order: 0 = prefix in the cache, 1 = prefix
 // tokens inside the chunk (n < P), 2 = still-visible ring (n > P), 3 = window tokens of
@@ -240,7 +233,8 @@ __device__ __forceinline__ void fetch_tile(const TileSrc& s, int seg, int t0, in
 
 
 template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const uint16_t* __restrict__ v_in,
+__global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const uint16_t* __restrict__ q_in,
+                                                              const uint16_t* __restrict__ v_in,
                                                               uint16_t* __restrict__ out,
                                                               float* __restrict__ lse, int chunk,
                                                               int n_qtiles,
@@ -285,10 +279,13 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     int row_pos[2];
     size_t q_off[2];
     bf16x8 qop[2][KS];
-    // RESET: prefix tiles come first and use the queries rotated at their renumbered
-    // positions; the operands are swapped once the walk leaves the prefix.
+    // Queries are rotated here, at the row's position, and scaled by scale * log2(e) so the
+    // softmax runs on exp2. RESET: prefix tiles come first and see the query rotated at its
+    // renumbered position, its index in the list [prefix, window] after the append
+    // (p inside the prefix, else P + min(w_b, p + 1 - wfloor) - 1); the operands are
+    // rotated again at p once the walk leaves the prefix.
     bool q_prefix = c.pe_mode == PSA_PE_RESET;
-    const uint16_t* stage_q = (const uint16_t*)(q_prefix ? c.stage_qp : c.stage_q);
+    const float q_sc = c.scale * kLog2e;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int r = 32 * wave + 16 * rb + l16;
@@ -296,9 +293,9 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
         const int g = r % G;
         row_pos[rb] = n + c0 + r / G;
         q_off[rb] = (((size_t)b * chunk + cl) * c.Hq + h * G + g) * D + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage_q + q_off[rb] + ks * 32));
+        const int p = n + cl;
+        const int pq = q_prefix && p >= c.pre[b] ? c.pre[b] + min(c.wlen[b], p + 1 - c.wfloor[b]) - 1 : p;
+        load_query<D>(qop[rb], q_in + q_off[rb], pq, c.inv_freq, lg, q_sc);
     }
 
     SoftmaxRows<DB> st;
@@ -365,12 +362,10 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
                 if (have_next) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
             }
             if (q_prefix && cseg >= 2) {
-                const uint16_t* sq = (const uint16_t*)c.stage_q;
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        qop[rb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(sq + q_off[rb] + ks * 32));
+                    load_query<D>(qop[rb], q_in + q_off[rb], n + min(row_pos[rb] - n, chunk - 1),
+                                  c.inv_freq, lg, q_sc);
                 q_prefix = false;
             }
             const int t1 = min(ct0 + kBN, wk.hi(cseg));
@@ -412,52 +407,53 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
 }
 
 template <int D, int G>
-hipError_t launch_g(const DevCache& c, const void* v, void* out, float* lse, int chunk, int cur,
-                    hipStream_t s) {
+hipError_t launch_g(const DevCache& c, const void* q, const void* v, void* out, float* lse,
+                    int chunk, int cur, hipStream_t s) {
     constexpr int BQ = kRows / G;
     const int n_qtiles = (chunk + BQ - 1) / BQ;
     const int total = n_qtiles * c.Hkv * c.B;
     const int grid = ((total + 7) / 8) * 8;
     if (c.Bs > 0)
         hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(grid), dim3(kPfBlock), 0, s, c,
-                           (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
+                           (const uint16_t*)q, (const uint16_t*)v, (uint16_t*)out, lse, chunk,
+                           n_qtiles, c.len[cur]);
     else
         hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(grid), dim3(kPfBlock), 0, s, c,
-                           (const uint16_t*)v, (uint16_t*)out, lse, chunk, n_qtiles, c.len[cur]);
+                           (const uint16_t*)q, (const uint16_t*)v, (uint16_t*)out, lse, chunk,
+                           n_qtiles, c.len[cur]);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const DevCache& c, const void* v, void* out, float* lse, int chunk, int cur,
-                    hipStream_t s) {
+hipError_t launch_d(const DevCache& c, const void* q, const void* v, void* out, float* lse,
+                    int chunk, int cur, hipStream_t s) {
     switch (c.Hq / c.Hkv) {
-        case 1: return launch_g<D, 1>(c, v, out, lse, chunk, cur, s);
-        case 2: return launch_g<D, 2>(c, v, out, lse, chunk, cur, s);
-        case 4: return launch_g<D, 4>(c, v, out, lse, chunk, cur, s);
-        default: return launch_g<D, 8>(c, v, out, lse, chunk, cur, s);
+        case 1: return launch_g<D, 1>(c, q, v, out, lse, chunk, cur, s);
+        case 2: return launch_g<D, 2>(c, q, v, out, lse, chunk, cur, s);
+        case 4: return launch_g<D, 4>(c, q, v, out, lse, chunk, cur, s);
+        default: return launch_g<D, 8>(c, q, v, out, lse, chunk, cur, s);
     }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_stage(const DevCache& c, const void* q, const void* k, int chunk, int cur,
-                                hipStream_t s) {
-    const int groups = (c.Hkv + c.Hq + kStageHeads - 1) / kStageHeads;
+hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur, hipStream_t s) {
+    const int groups = (c.Hkv + kStageHeads - 1) / kStageHeads;
     const size_t total = (size_t)c.B * chunk * groups * (c.D / 2);
     const dim3 grid((unsigned)((total + kBlock - 1) / kBlock));
     if (c.D == 128)
         hipLaunchKernelGGL((stage_chunk_kernel<128>), grid, dim3(kBlock), 0, s, c,
-                           (const uint16_t*)q, (const uint16_t*)k, chunk, c.len[cur]);
+                           (const uint16_t*)k, chunk, c.len[cur]);
     else
         hipLaunchKernelGGL((stage_chunk_kernel<64>), grid, dim3(kBlock), 0, s, c,
-                           (const uint16_t*)q, (const uint16_t*)k, chunk, c.len[cur]);
+                           (const uint16_t*)k, chunk, c.len[cur]);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const DevCache& c, const void* v, void* out, float* lse, int chunk,
-                          int cur, hipStream_t s) {
-    return c.D == 128 ? launch_d<128>(c, v, out, lse, chunk, cur, s)
-                      : launch_d<64>(c, v, out, lse, chunk, cur, s);
+hipError_t launch_prefill(const DevCache& c, const void* q, const void* v, void* out, float* lse,
+                          int chunk, int cur, hipStream_t s) {
+    return c.D == 128 ? launch_d<128>(c, q, v, out, lse, chunk, cur, s)
+                      : launch_d<64>(c, q, v, out, lse, chunk, cur, s);
 }
 
 }  // namespace psa

@@ -119,9 +119,6 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
     L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
     L->stage_k = off;  off = align_up(off + B * (size_t)d.max_chunk * Hkv * D * elem, A);
-    L->stage_q = off;  off = align_up(off + B * (size_t)d.max_chunk * Hq * D * 2, A);
-    L->stage_qp = off;
-    off = align_up(off + (d.pe_mode == PSA_PE_RESET ? B * (size_t)d.max_chunk * Hq * D * 2 : 0), A);
     L->total = off;
     L->S = (int32_t)S;
     L->elem = (int32_t)elem;
@@ -418,8 +415,6 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.part_o = (float*)(base + L.part_o);
     d.part_ml = (float*)(base + L.part_ml);
     d.stage_k = base + L.stage_k;
-    d.stage_q = base + L.stage_q;
-    d.stage_qp = base + L.stage_qp;
     d.B = desc->max_batch;
     d.Hq = desc->n_q_heads;
     d.Hkv = desc->n_kv_heads;
@@ -680,10 +675,10 @@ PSA_API int psa_prefill_attn(psa_cache* c, int32_t chunk, const void* q, const v
     if (mrc != PSA_OK) return mrc;
     const int cur = c->cur;
     int rc = timed(c, PSA_K_PREFILL_STAGE, s, "prefill stage",
-                   [&] { return psa::launch_prefill_stage(c->dev, q, k, chunk, cur, s); });
+                   [&] { return psa::launch_prefill_stage(c->dev, k, chunk, cur, s); });
     if (rc != PSA_OK) return rc;
     rc = timed(c, PSA_K_PREFILL, s, "prefill attention",
-               [&] { return psa::launch_prefill(c->dev, v, out, lse, chunk, cur, s); });
+               [&] { return psa::launch_prefill(c->dev, q, v, out, lse, chunk, cur, s); });
     if (rc != PSA_OK) return rc;
     rc = timed(c, PSA_K_APPEND, s, "prefill commit", [&] {
         return psa::launch_append(c->dev, c->dev.stage_k, v, chunk, chunk, 0, 1, cur, s);

@@ -31,8 +31,6 @@ struct DevCache {
     float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
     void* stage_k;       // [B][max_chunk][Hkv][D] rotated prefill-chunk keys (stored bytes)
-    void* stage_q;       // [B][max_chunk][Hq][D] rotated, scaled prefill-chunk queries (bf16)
-    void* stage_qp;      // same, rotated at the renumbered position for prefix keys (RESET)
     // W: ring slots per (sequence, head), the largest window any sequence may use
     int32_t B, Hq, Hkv, D, Pmax, W, S, dtype, max_chunk, max_splits, n_shared, shared_max, pe_mode;
     int32_t Bs, bshift, NBT, n_blocks;   // paged: block size (0: contiguous), log2, S / Bs
@@ -60,8 +58,7 @@ __device__ inline size_t kv_row(const DevCache& c, int b, int h, int slot) {
 
 
 struct Layout {
-    size_t k, v, pool_k, pool_v, tags, btab, state, inv_freq, part_o, part_ml, stage_k, stage_q,
-        stage_qp, total;
+    size_t k, v, pool_k, pool_v, tags, btab, state, inv_freq, part_o, part_ml, stage_k, total;
     int32_t S, elem, max_splits, n_blocks;
 };
 
@@ -134,12 +131,12 @@ __host__ __device__ inline int split_count(int n_pre, int n_win, int L, int pe_m
 int decode_resident_wgs(const DevCache& c);
 hipError_t launch_merge(const DevCache& c, void* out, float* lse, int split_tokens, int cur,
                         hipStream_t s);
-// Rotate a prefill chunk's keys (stored bytes) and queries (scaled, bf16) into the staging
-// buffers, then attend (bf16 storage only).
-hipError_t launch_prefill_stage(const DevCache& c, const void* q, const void* k, int chunk,
-                                int cur, hipStream_t s);
-hipError_t launch_prefill(const DevCache& c, const void* v, void* out, float* lse, int chunk,
-                          int cur, hipStream_t s);
+// Rotate a prefill chunk's keys into the staging buffer (the bytes the cache will hold),
+// then attend: the attention kernel rotates and scales the queries itself (bf16 storage
+// only).
+hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur, hipStream_t s);
+hipError_t launch_prefill(const DevCache& c, const void* q, const void* v, void* out, float* lse,
+                          int chunk, int cur, hipStream_t s);
 
 // Training attention (row space): forward writes out and lse; backward reads q, k, v,
 // out, lse, dout and writes dq, dk, dv (di: float32 workspace [B][T][Hq]).

@@ -1,7 +1,8 @@
-// Device helpers shared by every kernel that produces stored keys: the float64 rotation
-// at an absolute position and the single rounding to the storage type. The append kernel
-// and the prefill staging kernel both use these, so a chunk's keys attended by prefill are
-// byte-identical to the keys the cache then holds.
+// Rotary helpers. Stored keys: the float64 rotation at an absolute position and the single
+// rounding to the storage type; the append kernel and the prefill staging kernel both use
+// these, so a chunk's keys attended by prefill are byte-identical to the keys the cache
+// then holds. Queries (never stored): a float32 rotation of a float64-reduced angle, used
+// by the decode and prefill attention kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -61,6 +62,33 @@ __device__ __forceinline__ void rotate_with(double x, double y, double sn, doubl
     const double d = y * cs;
     *xr = a - b;
     *yr = c + d;
+}
+
+// Rotated, scaled query pair for position p (fp32 result). The angle p * theta_i is formed
+// and reduced modulo 2*pi in float64, then sin/cos are taken in float32: queries are never
+// stored, so float32 accuracy (~1e-7 relative) is all the logits need.
+__device__ __forceinline__ void rotate_query(float x, float y, int p, double theta, float sc,
+                                             float* xr, float* yr) {
+    const double phi = (double)p * theta;
+    const double two_pi = 6.283185307179586;
+    const double r = phi - two_pi * rint(phi * (1.0 / two_pi));
+    float sn, cs;
+    sincosf((float)r, &sn, &cs);
+    *xr = (x * cs - y * sn) * sc;
+    *yr = (x * sn + y * cs) * sc;
+}
+
+// The same rotation for queries that are rounded to bf16 afterwards (prefill): the angle is
+// reduced to a fraction of a turn in [-1/2, 1/2] in float64 and sin/cos come from the
+// hardware's sin(2 pi x) and cos(2 pi x) (absolute error of order 1e-6, far below the
+// bf16 rounding that follows).
+__device__ __forceinline__ void rotate_query_bf16(float x, float y, int p, double theta, float sc,
+                                                  float* xr, float* yr) {
+    const double turns = (double)p * theta * 0.15915494309189535;   // 1 / (2 pi)
+    const float fr = (float)(turns - rint(turns));
+    const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+    *xr = (x * cs - y * sn) * sc;
+    *yr = (x * sn + y * cs) * sc;
 }
 
 }  // namespace psa
