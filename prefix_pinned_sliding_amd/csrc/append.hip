@@ -129,49 +129,24 @@ __global__ __launch_bounds__(kBlock) void pool_load_kernel(DevCache c, int id, i
     V[dst + i + H] = v[src + i + H];
 }
 
-// One thread per (sequence b, token j, KV head h, rotation pair i): a one-token append is
-// latency-bound, so every pair gets its own thread (each computes its angle's sin/cos).
-// Token j of sequence b has position p = len[b] + j. Slot: p < P_b -> prefix slot p;
-// else ring slot P_max + (p - P_b) mod W. The window after the call is [wb', n') with
+// Where token j of sequence b goes when the sequence appends nb tokens (nb from the
+// launch). Token j has position p = len[b] + j. Slot: p < P_b -> prefix slot p; else ring
+// slot P_max + (p - P_b) mod W. The window after the call is [wb', n') with
 // wb' = max(wfloor, n' - w_b); a token older than wb' (dropped again within the call) is
-// not written, so the writer of each slot is unique. Window entries that the call drops
-// and whose slots no new token takes (possible when w_b < W) get tag -1: token j's thread
-// clears the j-th of them (there are at most n_b).
-template <int DT, int D>
-__global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typename Elem<DT>::T* k,
-                                                        const typename Elem<DT>::T* v, int n_stride,
-                                                        int n_uniform, int ragged, int k_rotated,
-                                                        const int32_t* __restrict__ len_cur,
-                                                        int32_t* __restrict__ len_next) {
-    using T = typename Elem<DT>::T;
-    constexpr int H = D / 2;
-    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    const size_t total = (size_t)c.B * n_stride * c.Hkv * H;
-    if (idx >= total) return;
-    const int i = (int)(idx % H);
-    size_t r = idx / H;
-    const int h = (int)(r % c.Hkv);
-    r /= c.Hkv;
-    const int j = (int)(r % n_stride);
-    const int b = (int)(r / n_stride);
-
-    // Inputs first (rows j < n_stride are always in the tensor): a store (length, tag, K)
-    // could alias them as far as the compiler knows, so a load issued after one would wait
-    // for it.
-    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * D;
-    const T kx = k[src + i], ky = k[src + i + H];
-    const T vx = v[src + i], vy = v[src + i + H];
-    const double theta = c.inv_freq[i];
-    const int nb = ragged ? c.nnew[b] : n_uniform;
-    const int L0 = len_cur[b];
-    if (j == 0 && h == 0 && i == 0) len_next[b] = L0 + nb;
-    if (j >= nb) return;
+// not written (slot -1), so the writer of each slot is unique. Window entries that the
+// call drops and whose slots no new token takes (possible when w_b < W) get tag -1: token
+// j clears the j-th of them (there are at most nb). Run by one thread of the token's block
+// (`lead`), which also writes the tag and, for j = 0, the new length.
+__device__ __forceinline__ int token_slot(const DevCache& c, int b, int j, int nb, int L0,
+                                          bool lead, int32_t* len_next) {
+    if (lead && j == 0) len_next[b] = L0 + nb;
+    if (j >= nb) return -1;
     const int p = L0 + j;
     const int P = c.pre[b];
     const int wf = c.wfloor[b], wl = c.wlen[b];
     const int n1 = L0 + nb;
     const int wb1 = max(wf, n1 - wl);                // window base after the call
-    if (h == 0 && i == 0 && wl < c.W) {
+    if (lead && wl < c.W) {
         const int e = max(wf, L0 - wl) + j;          // j-th entry leaving the window
         if (e < min(L0, wb1)) {
             const int d = (wb1 - e) % c.W;           // e's slot relative to wb1's, mod W
@@ -183,76 +158,82 @@ __global__ __launch_bounds__(kBlock) void append_kernel(DevCache c, const typena
     if (p < P) {
         slot = p;
     } else {
-        if (p < wb1) return;                         // dropped within this call
+        if (p < wb1) return -1;                      // dropped within this call
         slot = c.Pmax + (p - P) % c.W;
     }
-    const size_t dst = kv_rowidx(c, b, h, slot) * D;
-    T* K = (T*)c.k;
-    T* V = (T*)c.v;
-    if (k_rotated) {
-        K[dst + i] = kx;
-        K[dst + i + H] = ky;
-    } else {
-        double sn, cs, xr, yr;
-        angle_sincos(p, theta, &sn, &cs);
-        rotate_with(to_f64(kx), to_f64(ky), sn, cs, &xr, &yr);
-        K[dst + i] = store_as(xr, (T*)nullptr);
-        K[dst + i + H] = store_as(yr, (T*)nullptr);
+    if (lead) c.tags[(size_t)b * c.S + slot] = p;
+    return slot;
+}
+
+// One block per (token j, sequence b0 + blockIdx.y); its threads take the token's
+// (KV head h, rotation pair i) items, at most one per thread when H_kv * D / 2 <= 1024.
+// Each thread reads its inputs before its first store: a store could alias them as far as
+// the compiler knows, so a load issued after one would wait for it.
+template <int DT, int D>
+__global__ __launch_bounds__(1024) void append_kernel(DevCache c, const typename Elem<DT>::T* k,
+                                                      const typename Elem<DT>::T* v, int n_stride,
+                                                      int n_uniform, int ragged, int k_rotated,
+                                                      int b0, const int32_t* __restrict__ len_cur,
+                                                      int32_t* __restrict__ len_next) {
+    using T = typename Elem<DT>::T;
+    constexpr int H = D / 2;
+    const int j = blockIdx.x, b = b0 + blockIdx.y;
+    const int items = c.Hkv * H;
+    const size_t row0 = ((size_t)b * n_stride + j) * c.Hkv;   // input row of head 0
+    const int nb = ragged ? c.nnew[b] : n_uniform;
+    const int L0 = len_cur[b];
+    for (int t = threadIdx.x; t < items; t += blockDim.x) {
+        const int h = t / H, i = t % H;
+        const size_t src = (row0 + h) * D;
+        const T kx = k[src + i], ky = k[src + i + H];
+        const T vx = v[src + i], vy = v[src + i + H];
+        const double theta = c.inv_freq[i];
+        const int slot = token_slot(c, b, j, nb, L0, t == 0, len_next);
+        if (slot < 0) return;
+        const size_t dst = kv_rowidx(c, b, h, slot) * D;
+        T* K = (T*)c.k;
+        T* V = (T*)c.v;
+        if (k_rotated) {
+            K[dst + i] = kx;
+            K[dst + i + H] = ky;
+        } else {
+            double sn, cs, xr, yr;
+            angle_sincos(L0 + j, theta, &sn, &cs);
+            rotate_with(to_f64(kx), to_f64(ky), sn, cs, &xr, &yr);
+            K[dst + i] = store_as(xr, (T*)nullptr);
+            K[dst + i + H] = store_as(yr, (T*)nullptr);
+        }
+        V[dst + i] = vx;
+        V[dst + i + H] = vy;
     }
-    V[dst + i] = vx;
-    V[dst + i + H] = vy;
-    if (h == 0 && i == 0) c.tags[(size_t)b * c.S + slot] = p;
 }
 
 // Append of keys that are already rotated and rounded (a prefill chunk's staged keys) and
 // their values: the same slots, evictions and tags as append_kernel, moved 16 bytes at a
-// time. One thread per (sequence, token j, KV head, 16-byte chunk of a row).
+// time. One block per (token j, sequence b0 + blockIdx.y); its threads take the token's
+// (KV head, 16-byte chunk) items.
 template <int DT, int D>
-__global__ __launch_bounds__(kBlock) void commit_kernel(DevCache c, const uint32_t* k,
-                                                        const uint32_t* v, int n_stride,
-                                                        const int32_t* __restrict__ len_cur,
-                                                        int32_t* __restrict__ len_next) {
+__global__ __launch_bounds__(1024) void commit_kernel(DevCache c, const uint32_t* k,
+                                                      const uint32_t* v, int n_stride, int b0,
+                                                      const int32_t* __restrict__ len_cur,
+                                                      int32_t* __restrict__ len_next) {
     using T = typename Elem<DT>::T;
     constexpr int CPR = D * (int)sizeof(T) / 16;      // 16-byte chunks per row
-    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    const size_t total = (size_t)c.B * n_stride * c.Hkv * CPR;
-    if (idx >= total) return;
-    const int ch = (int)(idx % CPR);
-    size_t r = idx / CPR;
-    const int h = (int)(r % c.Hkv);
-    r /= c.Hkv;
-    const int j = (int)(r % n_stride);
-    const int b = (int)(r / n_stride);
-    const int nb = n_stride;
-    const size_t src = (((size_t)b * n_stride + j) * c.Hkv + h) * CPR + ch;
-    const u32x4 kk = reinterpret_cast<const u32x4*>(k)[src];   // before any store (see above)
-    const u32x4 vv = reinterpret_cast<const u32x4*>(v)[src];
+    const int j = blockIdx.x, b = b0 + blockIdx.y;
+    const int items = c.Hkv * CPR;
+    const size_t row0 = ((size_t)b * n_stride + j) * c.Hkv;
     const int L0 = len_cur[b];
-    if (j == 0 && h == 0 && ch == 0) len_next[b] = L0 + nb;
-    const int p = L0 + j;
-    const int P = c.pre[b];
-    const int wf = c.wfloor[b], wl = c.wlen[b];
-    const int n1 = L0 + nb;
-    const int wb1 = max(wf, n1 - wl);
-    if (h == 0 && ch == 0 && wl < c.W) {                 // as in append_kernel
-        const int e = max(wf, L0 - wl) + j;
-        if (e < min(L0, wb1)) {
-            const int d = (wb1 - e) % c.W;
-            const int rel = d == 0 ? 0 : c.W - d;
-            if (rel >= n1 - wb1) c.tags[(size_t)b * c.S + c.Pmax + (e - P) % c.W] = -1;
-        }
+    for (int t = threadIdx.x; t < items; t += blockDim.x) {
+        const int h = t / CPR, ch = t % CPR;
+        const size_t src = (row0 + h) * CPR + ch;
+        const u32x4 kk = reinterpret_cast<const u32x4*>(k)[src];   // before any store
+        const u32x4 vv = reinterpret_cast<const u32x4*>(v)[src];
+        const int slot = token_slot(c, b, j, n_stride, L0, t == 0, len_next);
+        if (slot < 0) return;
+        const size_t dst = kv_rowidx(c, b, h, slot) * CPR + ch;
+        reinterpret_cast<u32x4*>(c.k)[dst] = kk;
+        reinterpret_cast<u32x4*>(c.v)[dst] = vv;
     }
-    int slot;
-    if (p < P) {
-        slot = p;
-    } else {
-        if (p < wb1) return;
-        slot = c.Pmax + (p - P) % c.W;
-    }
-    const size_t dst = kv_rowidx(c, b, h, slot) * CPR + ch;
-    reinterpret_cast<u32x4*>(c.k)[dst] = kk;
-    reinterpret_cast<u32x4*>(c.v)[dst] = vv;
-    if (h == 0 && ch == 0) c.tags[(size_t)b * c.S + slot] = p;
 }
 
 inline unsigned blocks_for(size_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
@@ -320,34 +301,41 @@ hipError_t launch_pool_load(const DevCache& c, int id, int len, const void* k, c
 
 hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_stride,
                          int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s) {
-    if (k_rotated && !ragged && n_uniform == n_stride &&
-        (((uintptr_t)k | (uintptr_t)v) & 15u) == 0) {
-        const int cpr = c.D * (c.dtype == PSA_BF16 ? 2 : 4) / 16;
-        const size_t total = (size_t)c.B * n_stride * c.Hkv * cpr;
-#define PSA_COMMIT(DT, DD)                                                                    \
-    hipLaunchKernelGGL((commit_kernel<DT, DD>), dim3(blocks_for(total)), dim3(kBlock), 0, s, c, \
-                       (const uint32_t*)k, (const uint32_t*)v, n_stride, c.len[cur], c.len[cur ^ 1])
-        if (c.dtype == PSA_BF16) {
-            if (c.D == 128) PSA_COMMIT(PSA_BF16, 128); else PSA_COMMIT(PSA_BF16, 64);
-        } else {
-            if (c.D == 128) PSA_COMMIT(PSA_F32, 128); else PSA_COMMIT(PSA_F32, 64);
-        }
+    if (n_stride == 0) return hipSuccess;
+    const bool commit = k_rotated && !ragged && n_uniform == n_stride &&
+                        (((uintptr_t)k | (uintptr_t)v) & 15u) == 0;
+    const int per_row = commit ? c.D * (c.dtype == PSA_BF16 ? 2 : 4) / 16 : c.D / 2;
+    const int items = c.Hkv * per_row;
+    const int threads = items >= 1024 ? 1024 : (items + 63) / 64 * 64;
+    // grid: x = token, y = sequence (at most 65535 per launch)
+    for (int b0 = 0; b0 < c.B; b0 += 65535) {
+        const dim3 grid((unsigned)n_stride, (unsigned)(c.B - b0 < 65535 ? c.B - b0 : 65535));
+        if (commit) {
+#define PSA_COMMIT(DT, DD)                                                                   \
+    hipLaunchKernelGGL((commit_kernel<DT, DD>), grid, dim3(threads), 0, s, c, (const uint32_t*)k, \
+                       (const uint32_t*)v, n_stride, b0, c.len[cur], c.len[cur ^ 1])
+            if (c.dtype == PSA_BF16) {
+                if (c.D == 128) PSA_COMMIT(PSA_BF16, 128); else PSA_COMMIT(PSA_BF16, 64);
+            } else {
+                if (c.D == 128) PSA_COMMIT(PSA_F32, 128); else PSA_COMMIT(PSA_F32, 64);
+            }
 #undef PSA_COMMIT
-        return hipGetLastError();
-    }
-    const size_t total = (size_t)c.B * n_stride * c.Hkv * (c.D / 2);
-    const dim3 grid(blocks_for(total));
+        } else {
 #define PSA_APPEND(DT, DD)                                                                     \
-    hipLaunchKernelGGL((append_kernel<DT, DD>), grid, dim3(kBlock), 0, s, c,                   \
+    hipLaunchKernelGGL((append_kernel<DT, DD>), grid, dim3(threads), 0, s, c,                  \
                        (const typename Elem<DT>::T*)k, (const typename Elem<DT>::T*)v, n_stride, \
-                       n_uniform, ragged, k_rotated, c.len[cur], c.len[cur ^ 1])
-    if (c.dtype == PSA_BF16) {
-        if (c.D == 128) PSA_APPEND(PSA_BF16, 128); else PSA_APPEND(PSA_BF16, 64);
-    } else {
-        if (c.D == 128) PSA_APPEND(PSA_F32, 128); else PSA_APPEND(PSA_F32, 64);
-    }
+                       n_uniform, ragged, k_rotated, b0, c.len[cur], c.len[cur ^ 1])
+            if (c.dtype == PSA_BF16) {
+                if (c.D == 128) PSA_APPEND(PSA_BF16, 128); else PSA_APPEND(PSA_BF16, 64);
+            } else {
+                if (c.D == 128) PSA_APPEND(PSA_F32, 128); else PSA_APPEND(PSA_F32, 64);
+            }
 #undef PSA_APPEND
-    return hipGetLastError();
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace psa

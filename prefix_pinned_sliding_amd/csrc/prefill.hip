@@ -39,8 +39,6 @@ namespace psa {
 namespace {
 
 
-constexpr int kWaves = 4;                // staging kernel
-constexpr int kBlock = 64 * kWaves;
 constexpr int kPfWaves = 8;              // attention workgroup: two groups of 4 waves
 constexpr int kPfBlock = 64 * kPfWaves;
 constexpr int kRows = 32 * kPfWaves;     // rows (position x head) per workgroup
@@ -48,52 +46,49 @@ constexpr int kBN = kTileKeys;           // keys per tile
 constexpr int kNBuf = 3;                 // LDS tile buffers
 
 // Stage a chunk's keys: rotated at their absolute positions and rounded once (the bytes the
-// cache will hold). One thread per (sequence, token, group of kStageHeads KV heads, pair):
-// the angle's sin/cos is computed once per group. (Queries are rotated by the attention
-// kernel as it loads them.)
+// cache will hold). One block per (token j, sequence b0 + blockIdx.y); its threads take the
+// token's (group of kStageHeads KV heads, rotation pair) items, and each computes its
+// pair's sin/cos once for the group. (Queries are rotated by the attention kernel as it
+// loads them.)
 constexpr int kStageHeads = 4;
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void stage_chunk_kernel(DevCache c, const uint16_t* k,
-                                                             int chunk,
-                                                             const int32_t* __restrict__ len_cur) {
+__global__ __launch_bounds__(1024) void stage_chunk_kernel(DevCache c, const uint16_t* k, int chunk,
+                                                           int b0,
+                                                           const int32_t* __restrict__ len_cur) {
     constexpr int H = D / 2;
+    const int j = blockIdx.x, b = b0 + blockIdx.y;
     const int heads = c.Hkv;
     const int groups = (heads + kStageHeads - 1) / kStageHeads;
-    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    const size_t total = (size_t)c.B * chunk * groups * H;
-    if (idx >= total) return;
-    const int i = (int)(idx % H);
-    size_t r = idx / H;
-    const int grp = (int)(r % groups);
-    r /= groups;
-    const int j = (int)(r % chunk);
-    const int b = (int)(r / chunk);
-    const size_t tok = (size_t)b * chunk + j;
-    const int h0 = grp * kStageHeads;
-    // Every input element of the group is loaded before anything is stored: the staging
-    // buffer could alias the input as far as the compiler knows, so loads issued after a
-    // store would each wait for it. A group past the last head repeats it and stores nothing.
-    double xs[kStageHeads], ys[kStageHeads];
-    size_t offs[kStageHeads];
-#pragma unroll
-    for (int t = 0; t < kStageHeads; ++t) {
-        const int hh = min(h0 + t, heads - 1);
-        offs[t] = (tok * c.Hkv + hh) * D;
-        xs[t] = bf16_bits_to_f64(k[offs[t] + i]);
-        ys[t] = bf16_bits_to_f64(k[offs[t] + i + H]);
-    }
+    const size_t row0 = ((size_t)b * chunk + j) * c.Hkv;   // key row of head 0
     const int p = len_cur[b] + j;
-    double sn, cs;
-    angle_sincos(p, c.inv_freq[i], &sn, &cs);
     uint16_t* ko = (uint16_t*)c.stage_k;
+    for (int t = threadIdx.x; t < groups * H; t += blockDim.x) {
+        const int grp = t / H, i = t % H;
+        const int h0 = grp * kStageHeads;
+        // Every input element of the group is loaded before anything is stored: the staging
+        // buffer could alias the input as far as the compiler knows, so loads issued after a
+        // store would each wait for it. A group past the last head repeats it and stores
+        // nothing.
+        double xs[kStageHeads], ys[kStageHeads];
+        size_t offs[kStageHeads];
 #pragma unroll
-    for (int t = 0; t < kStageHeads; ++t) {
-        if (h0 + t >= heads) break;
-        double xr, yr;
-        rotate_with(xs[t], ys[t], sn, cs, &xr, &yr);
-        ko[offs[t] + i] = f64_to_bf16_bits(xr);
-        ko[offs[t] + i + H] = f64_to_bf16_bits(yr);
+        for (int u = 0; u < kStageHeads; ++u) {
+            const int hh = min(h0 + u, heads - 1);
+            offs[u] = (row0 + hh) * D;
+            xs[u] = bf16_bits_to_f64(k[offs[u] + i]);
+            ys[u] = bf16_bits_to_f64(k[offs[u] + i + H]);
+        }
+        double sn, cs;
+        angle_sincos(p, c.inv_freq[i], &sn, &cs);
+#pragma unroll
+        for (int u = 0; u < kStageHeads; ++u) {
+            if (h0 + u >= heads) break;
+            double xr, yr;
+            rotate_with(xs[u], ys[u], sn, cs, &xr, &yr);
+            ko[offs[u] + i] = f64_to_bf16_bits(xr);
+            ko[offs[u] + i + H] = f64_to_bf16_bits(yr);
+        }
     }
 }
 
@@ -438,16 +433,21 @@ hipError_t launch_d(const DevCache& c, const void* q, const void* v, void* out, 
 }  // namespace
 
 hipError_t launch_prefill_stage(const DevCache& c, const void* k, int chunk, int cur, hipStream_t s) {
-    const int groups = (c.Hkv + kStageHeads - 1) / kStageHeads;
-    const size_t total = (size_t)c.B * chunk * groups * (c.D / 2);
-    const dim3 grid((unsigned)((total + kBlock - 1) / kBlock));
-    if (c.D == 128)
-        hipLaunchKernelGGL((stage_chunk_kernel<128>), grid, dim3(kBlock), 0, s, c,
-                           (const uint16_t*)k, chunk, c.len[cur]);
-    else
-        hipLaunchKernelGGL((stage_chunk_kernel<64>), grid, dim3(kBlock), 0, s, c,
-                           (const uint16_t*)k, chunk, c.len[cur]);
-    return hipGetLastError();
+    const int items = (c.Hkv + kStageHeads - 1) / kStageHeads * (c.D / 2);
+    const int threads = items >= 1024 ? 1024 : (items + 63) / 64 * 64;
+    // grid: x = token, y = sequence (at most 65535 per launch)
+    for (int b0 = 0; b0 < c.B; b0 += 65535) {
+        const dim3 grid((unsigned)chunk, (unsigned)(c.B - b0 < 65535 ? c.B - b0 : 65535));
+        if (c.D == 128)
+            hipLaunchKernelGGL((stage_chunk_kernel<128>), grid, dim3(threads), 0, s, c,
+                               (const uint16_t*)k, chunk, b0, c.len[cur]);
+        else
+            hipLaunchKernelGGL((stage_chunk_kernel<64>), grid, dim3(threads), 0, s, c,
+                               (const uint16_t*)k, chunk, b0, c.len[cur]);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_prefill(const DevCache& c, const void* q, const void* v, void* out, float* lse,
