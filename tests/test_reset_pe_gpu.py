@@ -43,11 +43,14 @@ def test_decode_reset_phases(dtype, D, Hq, Hkv, split):
                                    atol=1e-5 if dtype == torch.float32 else 2e-2)
 
 
-def test_prefill_reset():
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (64, 32, 8), (128, 4, 4)])
+def test_prefill_reset(D, Hq, Hkv):
+    """Queries are rotated in the attention kernel: first at the renumbered position for
+    the prefix tiles, then again at p; both head dims and several group sizes."""
     W, C = 96, 128
     prefix = [40, 10, 0, 200]
     n_hist = [20, 300, 250, 260]
-    wl = configs.Workload("reset-pf", torch.bfloat16, 4, 16, 8, 128, W, prefix, [1] * 4, "prefill")
+    wl = configs.Workload("reset-pf", torch.bfloat16, 4, Hq, Hkv, D, W, prefix, [1] * 4, "prefill")
     c = drive.make_cache(wl, max_chunk=C, pe="reset")
     drive.fill(c, wl, n_hist)
     q = drive.query_block(wl, n_hist, C, "cuda")
