@@ -243,6 +243,17 @@ int psa_append(psa_cache *cache, const int32_t *n_new_host, int32_t n_uniform, c
  * scaled logits, or NULL. Errors: PSA_ERR_STATE if any sequence is empty. */
 int psa_decode_attn(psa_cache *cache, const void *q, void *out, float *lse, psa_stream stream);
 
+/* One step of the generation loop ([PS] 03: append the new token, then attend to the
+ * prefix and the window) in one decode launch: the same result, cache contents and state
+ * as psa_append(cache, NULL, 1, k, v, 1, stream) followed by psa_decode_attn(cache, q,
+ * out, lse, stream). k, v: [B][H_kv][D] (one token per sequence, as psa_append with
+ * n_stride = 1); q, out, lse as psa_decode_attn. Errors: PSA_ERR_ARG for a NULL k, v,
+ * q or out; PSA_ERR_STATE if a sequence was never reset or (paged) the pool has no free
+ * block for a token that needs one; PSA_ERR_OVERFLOW as psa_append. These leave the
+ * cache unchanged; PSA_ERR_HIP (a failed launch) may leave it advanced by the step. */
+int psa_decode_step(psa_cache *cache, const void *k, const void *v, const void *q, void *out,
+                    float *lse, psa_stream stream);
+
 /* Chunked prefill: every sequence takes `chunk` new tokens at positions
  * len_b .. len_b + chunk - 1; query row c (at p = len_b + c) attends to the prefix,
  * the window of p and the chunk's own tokens up to p (a chunk equals `chunk`

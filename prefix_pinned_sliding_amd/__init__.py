@@ -101,6 +101,7 @@ def _load() -> ctypes.CDLL:
         "psa_seq_blocks": (ctypes.c_int, [P, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "psa_append": (ctypes.c_int, [P, P, I32, P, P, I32, P]),
         "psa_decode_attn": (ctypes.c_int, [P, P, P, P, P]),
+        "psa_decode_step": (ctypes.c_int, [P, P, P, P, P, P, P]),
         "psa_prefill_attn": (ctypes.c_int, [P, I32, P, P, P, P, P, P]),
         "psa_export": (ctypes.c_int, [P, I32, P, P, P, ctypes.POINTER(I32), P]),
         "psa_seq_length": (I64, [P, I32]),
@@ -307,6 +308,25 @@ class Cache:
             raise ValueError("lse must be a contiguous float32 [B][H_q] tensor")
         _check(lib.psa_decode_attn(self._h, _ptr(q), _ptr(out), _ptr(lse), _stream(stream)),
                "psa_decode_attn")
+        return out
+
+    def decode_step(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+        """Append one token per sequence (k, v: [B][H_kv][D]) and decode it (q: [B][H_q][D])
+        in one launch; same result as append(k[:, None], v[:, None]) then decode(q)."""
+        for name, t in (("k", k), ("v", v)):
+            if t.dtype != self.dtype or not t.is_contiguous() or tuple(t.shape) != (self.B, self.Hkv, self.D):
+                raise ValueError(f"{name} must be a contiguous {self.dtype} [B][H_kv][D] tensor")
+        if q.dtype != self.dtype or not q.is_contiguous() or tuple(q.shape) != (self.B, self.Hq, self.D):
+            raise ValueError(f"q must be a contiguous {self.dtype} [B][H_q][D] tensor")
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (self.B, self.Hq)
+                                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 [B][H_q] tensor")
+        _check(lib.psa_decode_step(self._h, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(lse),
+                                   _stream(stream)), "psa_decode_step")
         return out
 
     def prefill(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

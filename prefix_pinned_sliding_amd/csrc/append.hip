@@ -129,42 +129,6 @@ __global__ __launch_bounds__(kBlock) void pool_load_kernel(DevCache c, int id, i
     V[dst + i + H] = v[src + i + H];
 }
 
-// Where token j of sequence b goes when the sequence appends nb tokens (nb from the
-// launch). Token j has position p = len[b] + j. Slot: p < P_b -> prefix slot p; else ring
-// slot P_max + (p - P_b) mod W. The window after the call is [wb', n') with
-// wb' = max(wfloor, n' - w_b); a token older than wb' (dropped again within the call) is
-// not written (slot -1), so the writer of each slot is unique. Window entries that the
-// call drops and whose slots no new token takes (possible when w_b < W) get tag -1: token
-// j clears the j-th of them (there are at most nb). Run by one thread of the token's block
-// (`lead`), which also writes the tag and, for j = 0, the new length.
-__device__ __forceinline__ int token_slot(const DevCache& c, int b, int j, int nb, int L0,
-                                          bool lead, int32_t* len_next) {
-    if (lead && j == 0) len_next[b] = L0 + nb;
-    if (j >= nb) return -1;
-    const int p = L0 + j;
-    const int P = c.pre[b];
-    const int wf = c.wfloor[b], wl = c.wlen[b];
-    const int n1 = L0 + nb;
-    const int wb1 = max(wf, n1 - wl);                // window base after the call
-    if (lead && wl < c.W) {
-        const int e = max(wf, L0 - wl) + j;          // j-th entry leaving the window
-        if (e < min(L0, wb1)) {
-            const int d = (wb1 - e) % c.W;           // e's slot relative to wb1's, mod W
-            const int rel = d == 0 ? 0 : c.W - d;
-            if (rel >= n1 - wb1) c.tags[(size_t)b * c.S + c.Pmax + (e - P) % c.W] = -1;
-        }
-    }
-    int slot;
-    if (p < P) {
-        slot = p;
-    } else {
-        if (p < wb1) return -1;                      // dropped within this call
-        slot = c.Pmax + (p - P) % c.W;
-    }
-    if (lead) c.tags[(size_t)b * c.S + slot] = p;
-    return slot;
-}
-
 // One block per (token j, sequence b0 + blockIdx.y); its threads take the token's
 // (KV head h, rotation pair i) items, at most one per thread when H_kv * D / 2 <= 1024.
 // Each thread reads its inputs before its first store: a store could alias them as far as

@@ -61,6 +61,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return (uint16_t)(u >> 16);
 }
 __device__ __forceinline__ uint16_t out_as(float x, uint16_t*) { return f32_to_bf16(x); }
+__device__ __forceinline__ uint16_t key_as(double x, uint16_t*) { return f64_to_bf16_bits(x); }
+__device__ __forceinline__ float key_as(double x, float*) { return (float)x; }
 __device__ __forceinline__ float out_as(float x, float*) { return x; }
 
 template <int CTRL>
@@ -113,11 +115,21 @@ struct KVTile {
     u32x4 k[U][CPL], v[U][CPL];
 };
 
+// With k_new != nullptr the launch first appends one token per sequence (k_new, v_new:
+// [B][H_kv][D], as append_kernel with one token) and then decodes it: the state is the one
+// after the append (n = len + 1). The new token's slot (the ring slot of the entry the
+// append evicts, or prefix slot n - 1) is one logical entry of exactly one split; that
+// split's workgroup writes the head's new key and value before it reads anything, and no
+// other workgroup reads the slot. (Once the ring is full it is read from slot 0, so the
+// new entry can sit in any split, not only the last.)
 template <int DT, int D, int G, int LPK, bool PAGED>
 __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
                                                                 const typename Elem<DT>::T* q,
                                                                 int split_tokens,
-                                                                const int32_t* __restrict__ len_cur) {
+                                                                const int32_t* __restrict__ len_cur,
+                                                                const typename Elem<DT>::T* k_new,
+                                                                const typename Elem<DT>::T* v_new,
+                                                                int32_t* __restrict__ len_next) {
     using T = typename Elem<DT>::T;
     constexpr int EPC = 16 / (int)sizeof(T);    // elements per 16-byte chunk
     constexpr int CPR = D / EPC;                // chunks per row
@@ -131,7 +143,8 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     using Tile = KVTile<DT, D, LPK, U>;
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int n = len_cur[b];
+    const bool fused = k_new != nullptr;
+    const int n = len_cur[b] + (fused ? 1 : 0);
     const SeqView sv = seq_view(c, b, n);
     const int n_pre = sv.n_pre, n_win = sv.n_win, ring_head = sv.head;
     const int Tb = n_pre + n_win;
@@ -215,10 +228,60 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
         }
     };
 
+    int owner = -1, i_new = 0;   // split holding the new token's entry (fused launch)
+    if (fused) {
+        const int p = n - 1, Pb = c.pre[b];
+        i_new = p;                                         // prefix slot p
+        if (p >= Pb) {
+            const int r = (p - Pb) % c.W;                  // its ring slot
+            i_new = n_pre + (r - ring_head + c.W) % c.W;
+        }
+        if (c.pe_mode == PSA_PE_RESET) {
+            const int ns_pre = (n_pre + split_tokens - 1) / split_tokens;
+            owner = i_new < n_pre ? i_new / split_tokens : ns_pre + (i_new - n_pre) / split_tokens;
+        } else {
+            owner = i_new / split_tokens;
+        }
+    }
+    // The owner appends this head's new token (position n - 1) as append_kernel does, on
+    // the last wave (the query set-up below runs on the first ones), then makes the stores
+    // visible to the workgroup's loads: a fence, and a barrier before any load that may
+    // reach the new entry. When the first batch of loads (entries [i0, i0 + STEP), the last
+    // one repeated past i1) cannot reach it, those loads go out first and the barrier after
+    // the query set-up serves; otherwise the append and a barrier come first.
+    auto append_new = [&](bool barrier) {
+        constexpr int H = D / 2;
+        const int t = tid - (kBlock - H);
+        if (t >= 0) {
+            const size_t src = ((size_t)b * c.Hkv + h) * D;
+            const T kx = k_new[src + t], ky = k_new[src + t + H];
+            const T vx = v_new[src + t], vy = v_new[src + t + H];
+            const double theta = c.inv_freq[t];
+            const int slot = token_slot(c, b, 0, 1, n - 1, h == 0 && t == 0, len_next);
+            if (slot >= 0) {
+                double sn, cs, xr, yr;
+                angle_sincos(n - 1, theta, &sn, &cs);
+                rotate_with(to_f64(kx), to_f64(ky), sn, cs, &xr, &yr);
+                const size_t dst = kv_rowidx(c, b, h, slot) * D;
+                T* K = (T*)c.k;
+                T* V = (T*)c.v;
+                K[dst + t] = key_as(xr, (T*)nullptr);
+                K[dst + t + H] = key_as(yr, (T*)nullptr);
+                V[dst + t] = vx;
+                V[dst + t + H] = vy;
+            }
+            __threadfence_block();
+        }
+        if (barrier) __syncthreads();
+    };
+    const bool append_first = split == owner && i_new < i0 + STEP;
+    if (append_first) append_new(true);
+
     // First K/V loads go out before the query set-up so that latency overlaps.
     int base_i = i0 + wave * KPW * U;
     Tile nxt;
     if (base_i < i1) load(nxt, base_i);
+    if (split == owner && !append_first) append_new(false);   // barrier: after the query set-up
 
     {
         const int p = qpos;
@@ -380,7 +443,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DevCache c, typename Elem<DT>:
 
 template <int DT, int D, int G>
 hipError_t launch_partial_g(const DevCache& c, const void* q, int split_tokens, int grid_splits,
-                            int cur, hipStream_t s) {
+                            int cur, const void* k_new, const void* v_new, hipStream_t s) {
+    using T = typename Elem<DT>::T;
     // Lanes per key: enough that q and the accumulators of G heads fit in registers,
     // never more than the 16-byte chunks in a row.
     constexpr int CPR = D / (16 / (int)sizeof(typename Elem<DT>::T));
@@ -389,21 +453,23 @@ hipError_t launch_partial_g(const DevCache& c, const void* q, int split_tokens, 
     const dim3 grid(grid_splits, c.Hkv, c.B);
     if (c.Bs > 0)
         hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK, true>), grid, dim3(kBlock), 0, s, c,
-                           (const typename Elem<DT>::T*)q, split_tokens, c.len[cur]);
+                           (const T*)q, split_tokens, c.len[cur], (const T*)k_new, (const T*)v_new,
+                           c.len[cur ^ 1]);
     else
         hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK, false>), grid, dim3(kBlock), 0, s, c,
-                           (const typename Elem<DT>::T*)q, split_tokens, c.len[cur]);
+                           (const T*)q, split_tokens, c.len[cur], (const T*)k_new, (const T*)v_new,
+                           c.len[cur ^ 1]);
     return hipGetLastError();
 }
 
 template <int DT, int D>
 hipError_t launch_partial_d(const DevCache& c, const void* q, int split_tokens, int grid_splits,
-                            int cur, hipStream_t s) {
+                            int cur, const void* k_new, const void* v_new, hipStream_t s) {
     switch (c.Hq / c.Hkv) {
-        case 1: return launch_partial_g<DT, D, 1>(c, q, split_tokens, grid_splits, cur, s);
-        case 2: return launch_partial_g<DT, D, 2>(c, q, split_tokens, grid_splits, cur, s);
-        case 4: return launch_partial_g<DT, D, 4>(c, q, split_tokens, grid_splits, cur, s);
-        default: return launch_partial_g<DT, D, 8>(c, q, split_tokens, grid_splits, cur, s);
+        case 1: return launch_partial_g<DT, D, 1>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s);
+        case 2: return launch_partial_g<DT, D, 2>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s);
+        case 4: return launch_partial_g<DT, D, 4>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s);
+        default: return launch_partial_g<DT, D, 8>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s);
     }
 }
 
@@ -438,12 +504,13 @@ int wgs_per_cu_d(int G) {
 }  // namespace
 
 hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
-                                 int grid_splits, int cur, hipStream_t s) {
+                                 int grid_splits, int cur, const void* k_new, const void* v_new,
+                                 hipStream_t s) {
     if (c.dtype == PSA_BF16)
-        return c.D == 128 ? launch_partial_d<PSA_BF16, 128>(c, q, split_tokens, grid_splits, cur, s)
-                          : launch_partial_d<PSA_BF16, 64>(c, q, split_tokens, grid_splits, cur, s);
-    return c.D == 128 ? launch_partial_d<PSA_F32, 128>(c, q, split_tokens, grid_splits, cur, s)
-                      : launch_partial_d<PSA_F32, 64>(c, q, split_tokens, grid_splits, cur, s);
+        return c.D == 128 ? launch_partial_d<PSA_BF16, 128>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s)
+                          : launch_partial_d<PSA_BF16, 64>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s);
+    return c.D == 128 ? launch_partial_d<PSA_F32, 128>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s)
+                      : launch_partial_d<PSA_F32, 64>(c, q, split_tokens, grid_splits, cur, k_new, v_new, s);
 }
 
 int decode_resident_wgs(const DevCache& c) {

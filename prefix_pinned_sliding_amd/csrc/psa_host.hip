@@ -650,11 +650,43 @@ PSA_API int psa_decode_attn(psa_cache* c, const void* q, void* out, float* lse, 
     hipStream_t s = (hipStream_t)stream;
     const int cur = c->cur;
     int rc = timed(c, PSA_K_DECODE, s, "decode partial", [&] {
-        return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, s);
+        return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, nullptr, nullptr, s);
     });
     if (rc != PSA_OK) return rc;
     return timed(c, PSA_K_MERGE, s, "split merge",
                  [&] { return psa::launch_merge(c->dev, out, lse, L, cur, s); });
+}
+
+PSA_API int psa_decode_step(psa_cache* c, const void* k, const void* v, const void* q, void* out,
+                            float* lse, psa_stream stream) {
+    if (c == nullptr) return fail(PSA_ERR_ARG, "cache is NULL");
+    if (k == nullptr || v == nullptr || q == nullptr || out == nullptr)
+        return fail(PSA_ERR_ARG, "k, v, q or out is NULL");
+    const int B = c->desc.max_batch;
+    for (int b = 0; b < B; ++b) {
+        if (c->pre[b] < 0) return fail(PSA_ERR_STATE, "decode step on a sequence that was never reset");
+        if (c->len[b] + 1 > INT32_MAX) return fail(PSA_ERR_OVERFLOW, "sequence length overflow");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int mrc = map_append(c, nullptr, 1, s);
+    if (mrc != PSA_OK) return mrc;
+    // Split planning sees the state after the append, as psa_decode_attn would.
+    for (int b = 0; b < B; ++b) c->len[b] += 1;
+    const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
+    int64_t max_ns = 1;
+    for (int b = 0; b < B; ++b) {
+        const psa::SeqView sv = view_of(c, b);
+        const int64_t ns = psa::split_count(sv.n_pre, sv.n_win, L, c->desc.pe_mode);
+        if (ns > max_ns) max_ns = ns;
+    }
+    const int cur = c->cur;
+    c->cur ^= 1;
+    int rc = timed(c, PSA_K_DECODE, s, "decode step", [&] {
+        return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, k, v, s);
+    });
+    if (rc != PSA_OK) return rc;
+    return timed(c, PSA_K_MERGE, s, "split merge",
+                 [&] { return psa::launch_merge(c->dev, out, lse, L, cur ^ 1, s); });
 }
 
 PSA_API int psa_prefill_attn(psa_cache* c, int32_t chunk, const void* q, const void* k,

@@ -92,6 +92,42 @@ __device__ inline SeqView seq_view(const DevCache& c, int b, int n) {
     return seq_view(n, c.pre[b], c.npin[b], c.wfloor[b], c.wlen[b], c.W);
 }
 
+// Where token j of sequence b goes when the sequence appends nb tokens (nb from the
+// launch). Token j has position p = len[b] + j. Slot: p < P_b -> prefix slot p; else ring
+// slot P_max + (p - P_b) mod W. The window after the call is [wb', n') with
+// wb' = max(wfloor, n' - w_b); a token older than wb' (dropped again within the call) is
+// not written (slot -1), so the writer of each slot is unique. Window entries that the
+// call drops and whose slots no new token takes (possible when w_b < W) get tag -1: token
+// j clears the j-th of them (there are at most nb). Run by one thread of the token's block
+// (`lead`), which also writes the tag and, for j = 0, the new length.
+__device__ inline int token_slot(const DevCache& c, int b, int j, int nb, int L0,
+                                          bool lead, int32_t* len_next) {
+    if (lead && j == 0) len_next[b] = L0 + nb;
+    if (j >= nb) return -1;
+    const int p = L0 + j;
+    const int P = c.pre[b];
+    const int wf = c.wfloor[b], wl = c.wlen[b];
+    const int n1 = L0 + nb;
+    const int wb1 = max(wf, n1 - wl);                // window base after the call
+    if (lead && wl < c.W) {
+        const int e = max(wf, L0 - wl) + j;          // j-th entry leaving the window
+        if (e < min(L0, wb1)) {
+            const int d = (wb1 - e) % c.W;           // e's slot relative to wb1's, mod W
+            const int rel = d == 0 ? 0 : c.W - d;
+            if (rel >= n1 - wb1) c.tags[(size_t)b * c.S + c.Pmax + (e - P) % c.W] = -1;
+        }
+    }
+    int slot;
+    if (p < P) {
+        slot = p;
+    } else {
+        if (p < wb1) return -1;                      // dropped within this call
+        slot = c.Pmax + (p - P) % c.W;
+    }
+    if (lead) c.tags[(size_t)b * c.S + slot] = p;
+    return slot;
+}
+
 // Kernel launchers (stream-ordered, asynchronous). They return the launch status.
 hipError_t launch_init(const DevCache& c, hipStream_t s);
 // Write n (<= kTableUpdates) block-table entries: btab[idx[i]] = blk[i].
@@ -117,8 +153,12 @@ hipError_t launch_pool_load(const DevCache& c, int id, int len, const void* k, c
 // k/v: [B][n_stride][Hkv][D]; k_rotated != 0 means k already holds rotated, rounded keys.
 hipError_t launch_append(const DevCache& c, const void* k, const void* v, int n_stride,
                          int n_uniform, int ragged, int k_rotated, int cur, hipStream_t s);
+// Decode partials over the state len[cur]; with k_new != nullptr, first append one token
+// per sequence (k_new, v_new: [B][Hkv][D]) and decode over len[cur] + 1, writing the new
+// lengths to len[cur ^ 1].
 hipError_t launch_decode_partial(const DevCache& c, const void* q, int split_tokens,
-                                 int grid_splits, int cur, hipStream_t s);
+                                 int grid_splits, int cur, const void* k_new, const void* v_new,
+                                 hipStream_t s);
 // Decode splits of a sequence with n_pre prefix and n_win window entries. CONTINUE cuts the
 // concatenated list; RESET cuts the prefix and the window separately, so a split never
 // mixes keys that need differently rotated queries.

@@ -25,7 +25,7 @@ def psa():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["psa_cache_bytes", "psa_cache_create", "psa_cache_destroy", "psa_seq_reset",
-                 "psa_append", "psa_decode_attn", "psa_prefill_attn", "psa_export",
+                 "psa_append", "psa_decode_attn", "psa_decode_step", "psa_prefill_attn", "psa_export",
                  "psa_seq_length", "psa_status_string", "psa_last_error"]:
         assert want in names
 
@@ -141,6 +141,7 @@ def test_null_handle_calls(psa):
     assert lib.psa_seq_reset(None, 0, 0, None) == psa.PSA_ERR_ARG
     assert lib.psa_append(None, None, 1, None, None, 1, None) == psa.PSA_ERR_ARG
     assert lib.psa_decode_attn(None, None, None, None, None) == psa.PSA_ERR_ARG
+    assert lib.psa_decode_step(None, None, None, None, None, None, None) == psa.PSA_ERR_ARG
     assert lib.psa_prefill_attn(None, 1, None, None, None, None, None, None) == psa.PSA_ERR_ARG
     cnt = ctypes.c_int32()
     assert lib.psa_export(None, 0, None, None, None, ctypes.byref(cnt), None) == psa.PSA_ERR_ARG
