@@ -27,13 +27,16 @@ __device__ __forceinline__ uint16_t store_as(double x, uint16_t*) { return f64_t
 __device__ __forceinline__ float store_as(double x, float*) { return (float)x; }
 
 // Tags -1; lengths, prefix lengths and token counts 0; prefix entries -1 (own prefix);
-// block-table entries -1 (paged).
+// decode order the identity; block-table entries -1 (paged).
 __global__ void init_kernel(int32_t* tags, size_t n_tags, int32_t* state, int n_zero,
-                            int32_t* pid, int B, int32_t* btab, size_t n_btab) {
+                            int32_t* pid, int32_t* order, int B, int32_t* btab, size_t n_btab) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_tags) tags[i] = -1;
     if (i < (size_t)n_zero) state[i] = 0;
-    if (i < (size_t)B) pid[i] = -1;
+    if (i < (size_t)B) {
+        pid[i] = -1;
+        order[i] = (int32_t)i;
+    }
     if (i < n_btab) btab[i] = -1;
 }
 
@@ -212,13 +215,19 @@ hipError_t launch_init(const DevCache& c, hipStream_t s) {
     const size_t n_btab = (size_t)c.B * c.NBT;
     const size_t m = n > n_btab ? n : n_btab;
     hipLaunchKernelGGL(init_kernel, dim3(blocks_for(m)), dim3(kBlock), 0, s, c.tags, n_tags,
-                       c.len[0], n_zero, c.pid, c.B, c.btab, n_btab);
+                       c.len[0], n_zero, c.pid, c.order, c.B, c.btab, n_btab);
     return hipGetLastError();
 }
 
 hipError_t launch_table_update(const DevCache& c, const TableUpdate& u, hipStream_t s) {
     if (u.n <= 0) return hipSuccess;
     hipLaunchKernelGGL(table_update_kernel, dim3(1), dim3(kTableUpdates), 0, s, c.btab, u);
+    return hipGetLastError();
+}
+
+hipError_t launch_order_update(const DevCache& c, const TableUpdate& u, hipStream_t s) {
+    if (u.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(table_update_kernel, dim3(1), dim3(kTableUpdates), 0, s, c.order, u);
     return hipGetLastError();
 }
 

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     static_assert(CPL >= 1 && CPR % LPK == 0, "lane layout");
     using Tile = KVTile<DT, D, LPK, U>;
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x, h = blockIdx.y, b = c.order[blockIdx.z];
     const bool fused = k_new != nullptr;
     const int n = len_cur[b] + (fused ? 1 : 0);
     const SeqView sv = seq_view(c, b, n);

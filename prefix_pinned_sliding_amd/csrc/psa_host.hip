@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -48,6 +49,7 @@ struct psa_cache {
     std::vector<int32_t> attached; // sequences attached to each pool entry
     std::vector<int32_t> btab;     // paged: host copy of the block table [B][NBT]
     std::vector<int32_t> free_blk; // paged: unused physical blocks (a stack)
+    std::vector<int32_t> order;    // decode workgroup order on the device (grid z -> sequence)
     int32_t split_tokens;          // 0 = automatic
     int resident_wgs;              // decode workgroups resident at once (0 = not yet queried)
     bool profiling;
@@ -114,7 +116,7 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     L->pool_v = off;   off = align_up(off + pool, A);
     L->tags = off;     off = align_up(off + B * (size_t)S * 4, A);
     L->btab = off;     off = align_up(off + (d.block_size ? B * (size_t)(S / d.block_size) * 4 : 0), A);
-    L->state = off;    off = align_up(off + 8 * B * 4, A);
+    L->state = off;    off = align_up(off + 9 * B * 4, A);
     L->inv_freq = off; off = align_up(off + D / 2 * 8, A);
     L->part_o = off;   off = align_up(off + B * Hq * (size_t)max_splits * D * 4, A);
     L->part_ml = off;  off = align_up(off + B * Hq * (size_t)max_splits * 2 * 4, A);
@@ -208,6 +210,39 @@ int auto_split_tokens(psa_cache* c) {
 }
 
 bool valid_seq(const psa_cache* c, int32_t seq) { return seq >= 0 && seq < c->desc.max_batch; }
+
+// Decode workgroups go out sequence by sequence in the device order array (grid z); with
+// sequences of different lengths, the longest first, so the short ones fill the end of
+// the launch instead of a long one running alone. Sequences are ranked by visible entries
+// in units of kSplitGranule (ties in index order), so steady decoding, which adds one
+// entry at a time, rarely changes the order; the entries that change are written by one
+// small launch per kTableUpdates of them.
+int update_decode_order(psa_cache* c, hipStream_t s) {
+    const int B = c->desc.max_batch;
+    std::vector<int64_t> key(B);
+    for (int b = 0; b < B; ++b) key[b] = visible_count(c, b) / psa::kSplitGranule;
+    std::vector<int32_t> want(B);
+    for (int b = 0; b < B; ++b) want[b] = b;
+    std::stable_sort(want.begin(), want.end(), [&](int32_t x, int32_t y) { return key[x] > key[y]; });
+    psa::TableUpdate u;
+    u.n = 0;
+    for (int z = 0; z < B; ++z) {
+        if (want[z] == c->order[z]) continue;
+        u.idx[u.n] = z;
+        u.blk[u.n] = want[z];
+        if (++u.n == psa::kTableUpdates) {
+            const hipError_t e = psa::launch_order_update(c->dev, u, s);
+            if (e != hipSuccess) return hip_fail(e, "decode order update");
+            u.n = 0;
+        }
+    }
+    if (u.n > 0) {
+        const hipError_t e = psa::launch_order_update(c->dev, u, s);
+        if (e != hipSuccess) return hip_fail(e, "decode order update");
+    }
+    c->order = want;
+    return PSA_OK;
+}
 
 // ---- paged caches: the host's block allocator -------------------------------------------
 // Logical block j of sequence b covers slots [j * Bs, (j + 1) * Bs); the device table gets
@@ -389,6 +424,8 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     c->attached.assign(desc->n_shared_prefixes, 0);
     c->split_tokens = 0;
     c->resident_wgs = 0;
+    c->order.resize(desc->max_batch);
+    for (int b = 0; b < desc->max_batch; ++b) c->order[b] = b;   // init_kernel's order
     c->profiling = false;
     for (int i = 0; i < PSA_K_COUNT; ++i) {
         c->total_ms[i] = 0.0;
@@ -411,6 +448,7 @@ PSA_API int psa_cache_create(const psa_cache_desc* desc, void* dev_mem, size_t b
     d.npin = st + 5 * desc->max_batch;
     d.wfloor = st + 6 * desc->max_batch;
     d.wlen = st + 7 * desc->max_batch;
+    d.order = st + 8 * desc->max_batch;
     d.inv_freq = (double*)(base + L.inv_freq);
     d.part_o = (float*)(base + L.part_o);
     d.part_ml = (float*)(base + L.part_ml);
@@ -648,6 +686,8 @@ PSA_API int psa_decode_attn(psa_cache* c, const void* q, void* out, float* lse, 
         if (ns > max_ns) max_ns = ns;
     }
     hipStream_t s = (hipStream_t)stream;
+    const int orc = update_decode_order(c, s);
+    if (orc != PSA_OK) return orc;
     const int cur = c->cur;
     int rc = timed(c, PSA_K_DECODE, s, "decode partial", [&] {
         return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, nullptr, nullptr, s);
@@ -679,6 +719,8 @@ PSA_API int psa_decode_step(psa_cache* c, const void* k, const void* v, const vo
         const int64_t ns = psa::split_count(sv.n_pre, sv.n_win, L, c->desc.pe_mode);
         if (ns > max_ns) max_ns = ns;
     }
+    const int orc = update_decode_order(c, s);
+    if (orc != PSA_OK) return orc;
     const int cur = c->cur;
     c->cur ^= 1;
     int rc = timed(c, PSA_K_DECODE, s, "decode step", [&] {

@@ -27,6 +27,7 @@ struct DevCache {
     int32_t* npin;       // [B] pinned entries once the prefix is complete (P_b + promoted)
     int32_t* wfloor;     // [B] no window entry is older than this position
     int32_t* wlen;       // [B] the sequence's window length w_b (<= W)
+    int32_t* order;      // [B] decode workgroup order: grid index z -> sequence (longest first)
     double* inv_freq;    // [D/2] theta_i
     float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
@@ -137,6 +138,8 @@ struct TableUpdate {
     int32_t blk[kTableUpdates];
 };
 hipError_t launch_table_update(const DevCache& c, const TableUpdate& u, hipStream_t s);
+// The same for the decode order: order[idx[i]] = blk[i] (blk holds sequence indices).
+hipError_t launch_order_update(const DevCache& c, const TableUpdate& u, hipStream_t s);
 // Start a sequence: tags -1, length `len0`, prefix length `prefix_len`, prefix entry `pid`.
 hipError_t launch_seq_reset(const DevCache& c, int seq, int prefix_len, int len0, int pid, int cur,
                             hipStream_t s);
