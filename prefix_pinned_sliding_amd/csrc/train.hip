@@ -24,6 +24,7 @@
 namespace psa {
 namespace {
 
+
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kBN = 64;      // keys per tile
@@ -143,7 +144,10 @@ __global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, in
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
     if (logical >= total) return;
-    const int qt = logical % n_qtiles, bh = logical / n_qtiles;
+    // query tiles of one (sequence, KV head) go out last first: rows in the first window see
+    // fewer keys, so the longest tiles start first and the short ones fill the end
+    const int qt = n_qtiles - 1 - logical % n_qtiles;
+    const int bh = logical / n_qtiles;
     const int h = bh % a.Hkv, b = bh / a.Hkv;
     const int len = a.len[b], P = a.pre[b], W = a.W;
     const int c0 = qt * BQ;
@@ -403,7 +407,10 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
     if (logical >= total) return;
-    const int qt = logical % n_qtiles, bh = logical / n_qtiles;
+    // query tiles of one (sequence, KV head) go out last first: rows in the first window see
+    // fewer keys, so the longest tiles start first and the short ones fill the end
+    const int qt = n_qtiles - 1 - logical % n_qtiles;
+    const int bh = logical / n_qtiles;
     const int h = bh % a.Hkv, b = bh / a.Hkv;
     const int len = a.len[b], P = a.pre[b], W = a.W;
     const int c0 = qt * BQ;
