@@ -25,6 +25,7 @@ namespace psa {
 namespace {
 
 
+
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kBN = 64;      // keys per tile
@@ -280,7 +281,20 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
     const int total = n_ktiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
     if (logical >= total) return;
-    const int kt = logical % n_ktiles, bh = logical / n_ktiles;
+    int kt = logical % n_ktiles, bh = logical / n_ktiles;
+    // When every XCD holds whole (sequence, KV head) ranges, take them key tile by key
+    // tile across its pairs: the prefix tiles, which every query row sees, start first on
+    // all pairs.
+    {
+        const int nbh = a.Hkv * a.B;
+        if (nbh % 8 == 0) {
+            const int per = nbh / 8;                       // pairs per XCD
+            const int x = logical / (per * n_ktiles);      // this XCD's range
+            const int j = logical % (per * n_ktiles);      // place in its dispatch order
+            kt = j / per;
+            bh = x * per + j % per;
+        }
+    }
     const int h = bh % a.Hkv, b = bh / a.Hkv;
     const int len = a.len[b], P = a.pre[b], W = a.W;
     const int k0 = kt * kBN;
