@@ -190,7 +190,8 @@ int64_t visible_count(const psa_cache* c, int b) {
 // and splitting long sequences would only add uneven pieces. With fewer pairs the batch
 // must be split for parallelism, and ref is the mean length, so that the pieces of a
 // ragged batch add up to about two rounds instead of leaving short sequences' workgroups
-// underfilled. Never shorter than kSplitGranule entries.
+// underfilled; then the length is raised, if needed, to the shortest that keeps the grid
+// within two full rounds. Never shorter than kSplitGranule entries.
 int auto_split_tokens(psa_cache* c) {
     int64_t longest = 1, sum = 0;
     for (int b = 0; b < c->desc.max_batch; ++b) {
@@ -201,11 +202,37 @@ int auto_split_tokens(psa_cache* c) {
     if (c->resident_wgs == 0) c->resident_wgs = psa::decode_resident_wgs(c->dev);
     const int64_t pairs = (int64_t)c->desc.max_batch * c->desc.n_kv_heads;
     const int64_t mean = (sum + c->desc.max_batch - 1) / c->desc.max_batch;
-    const int64_t ref = pairs < c->resident_wgs && mean > 0 ? mean : longest;
+    const bool few_pairs = pairs < c->resident_wgs && mean > 0;
+    const int64_t ref = few_pairs ? mean : longest;
     int64_t ns = (2 * (int64_t)c->resident_wgs) / pairs;
     if (ns < 1) ns = 1;
     int64_t L = (ref + ns - 1) / ns;
     if (L < psa::kSplitGranule) L = psa::kSplitGranule;
+    if (few_pairs) {
+        // Each sequence's last split is partial, so pieces of the mean length add up to
+        // more than two rounds (half a workgroup per sequence on average). Lengthen the
+        // splits to the shortest that keeps the grid within two full rounds (the count
+        // only falls as L grows, so a bisection finds it).
+        const int64_t budget = 2 * (int64_t)c->resident_wgs;
+        auto wgs = [&](int64_t len) {
+            int64_t n = 0;
+            for (int b = 0; b < c->desc.max_batch; ++b) {
+                const psa::SeqView v = view_of(c, b);
+                n += psa::split_count(v.n_pre, v.n_win, (int)len, c->desc.pe_mode);
+            }
+            return n * c->desc.n_kv_heads;
+        };
+        if (wgs(L) > budget) {
+            int64_t lo = L, hi = longest > L ? longest : L;   // wgs(hi) is the fewest
+            if (wgs(hi) <= budget) {
+                while (lo + 1 < hi) {
+                    const int64_t mid = (lo + hi) / 2;
+                    if (wgs(mid) <= budget) hi = mid; else lo = mid;
+                }
+                L = hi;
+            }
+        }
+    }
     return (int)L;
 }
 
