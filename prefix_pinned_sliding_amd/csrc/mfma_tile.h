@@ -100,8 +100,9 @@ struct SoftmaxRows {
 };
 
 // The three phases of one 64-key tile for a wave's 32 rows. tile_qk: S^T = K Q^T - mb.
-// tile_softmax: the mask (edge tiles only), the running-max update (rescaling O and l when
-// it moves), P^T = exp2(S^T) as bf16 B operands. tile_pv: l += 1 P^T and O^T += V^T P^T.
+// tile_softmax: tile_max (the mask, edge tiles only, and the running-max update, rescaling
+// O and l when it moves), then P^T = exp2(S^T) as bf16 B operands. tile_pv: l += 1 P^T and
+// O^T += V^T P^T.
 //
 // `sc` converts products to the log2 domain: 1 when the queries were loaded already scaled
 // by scale * log2(e) (prefill), scale * log2(e) otherwise (training). The accumulators
@@ -142,11 +143,11 @@ __device__ __forceinline__ void tile_qk(f32x4 (&s)[2][kTileKeys / 16], const Sof
 }
 
 template <int D>
-__device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][kTileKeys / 32], f32x4 (&s)[2][kTileKeys / 16],
-                                             SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
-                                             int ct0, int t1, int P, int W, int lg, bool masked,
-                                             float sc, float inv_sc) {
-    constexpr int DB = D / 16, KB = kTileKeys / 16, PVS = kTileKeys / 32;
+__device__ __forceinline__ void tile_max(f32x4 (&s)[2][kTileKeys / 16],
+                                         SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
+                                         int ct0, int t1, int P, int W, int lg, bool masked,
+                                         float sc, float inv_sc) {
+    constexpr int DB = D / 16, KB = kTileKeys / 16;
     // Masked logits become -inf: exp2(-inf) is 0 for any finite shift.
     float ml[2];
 #pragma unroll
@@ -192,6 +193,15 @@ __device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][kTileKeys / 32], f3
             }
         }
     }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][kTileKeys / 32], f32x4 (&s)[2][kTileKeys / 16],
+                                             SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
+                                             int ct0, int t1, int P, int W, int lg, bool masked,
+                                             float sc, float inv_sc) {
+    constexpr int PVS = kTileKeys / 32;
+    tile_max<D>(s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -228,9 +238,62 @@ __device__ __forceinline__ void tile_pv(SoftmaxRows<D / 16>& st, const bf16x8 (&
         }
 }
 
-// One whole tile: the three phases in order, with an optional workgroup barrier between
-// the products S^T and the softmax.
+// The exponentials and products of one tile, 32 keys at a time. The wave issues in order
+// (scheduling barriers fix it): the first step's V^T reads and exponentials, then the first
+// step's products with one exponential of the second step (and the second step's V^T
+// reads) between consecutive products, so that VALU work runs while the matrix core is
+// busy, then the second step's products.
 template <int D>
+__device__ __forceinline__ void tile_exp_pv(SoftmaxRows<D / 16>& st, const f32x4 (&s)[2][kTileKeys / 16],
+                                            const uint16_t* v_s, int l16, int lg, float sc) {
+    constexpr int DB = D / 16, PVS = kTileKeys / 32;
+    constexpr int VSTR = D + kVPad;
+    static_assert(PVS == 2 && DB >= 4, "two 32-key steps per tile, at least 16 products each");
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    const uint16_t* vrow = v_s + (4 * lg + l16 / 4) * VSTR + 4 * (l16 % 4);
+    bf16x8 va[2][DB];
+    bf16x8 pb[2][PVS];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[0][db] = lds_read_tr2(vrow + db * 16, vrow + 16 * VSTR + db * 16);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pb[rb][0][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][0][i] * sc);
+            pb[rb][0][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][1][i] * sc);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][0], st.l[0], 0, 0, 0);
+    st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][0], st.l[1], 0, 0, 0);
+    // 16 exponentials of the second step over the first step's 2 DB products
+    constexpr int PER = 16 / DB;   // exponentials per db (two products)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][db], pb[0][0], st.o[0][db], 0, 0, 0);
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][db], pb[1][0], st.o[1][db], 0, 0, 0);
+#pragma unroll
+        for (int e = db * PER; e < (db + 1) * PER; ++e) {
+            const int rb = e / 8, i = e % 8;
+            pb[rb][1][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 + i / 4][i % 4] * sc);
+        }
+        va[1][db] = lds_read_tr2(vrow + 32 * VSTR + db * 16, vrow + 48 * VSTR + db * 16);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][1], st.l[0], 0, 0, 0);
+    st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][1], st.l[1], 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][db], pb[0][1], st.o[0][db], 0, 0, 0);
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][db], pb[1][1], st.o[1][db], 0, 0, 0);
+    }
+}
+
+// One whole tile: the three phases in order, with an optional workgroup barrier between
+// the products S^T and the softmax. With kSplitExp the exponentials and products run 32
+// keys at a time (tile_exp_pv); it pays where the products arrive in the log2 domain
+// (sc = 1): about 1% on the prefill kernel, and 3% slower on the training forward pass.
+template <int D, bool kSplitExp = false>
 __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
                                           const uint16_t* k_s, const uint16_t* v_s,
                                           const int (&row_pos)[2], int ct0, int t1, int P, int W,
@@ -239,9 +302,14 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
     f32x4 s[2][kTileKeys / 16];
     tile_qk<D>(s, st, qop, k_s, l16, lg, inv_sc);
     if (mid_barrier) __syncthreads();
-    bf16x8 pb[2][kTileKeys / 32];
-    tile_softmax<D>(pb, s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
-    tile_pv<D>(st, pb, v_s, l16, lg);
+    if constexpr (kSplitExp) {
+        tile_max<D>(s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
+        tile_exp_pv<D>(st, s, v_s, l16, lg, sc);
+    } else {
+        bf16x8 pb[2][kTileKeys / 32];
+        tile_softmax<D>(pb, s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
+        tile_pv<D>(st, pb, v_s, l16, lg);
+    }
 }
 
 }  // namespace

@@ -366,8 +366,8 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
             const int t1 = min(ct0 + kBN, wk.hi(cseg));
             const bool full = (ct0 + kBN == t1) && (t1 - 1 <= p_lo) &&
                               (t1 - 1 < P || ct0 >= p_hi - W + 1);
-            tile_step<D>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, t1, P, W, l16, lg, !full, grp_b,
-                         1.f, 1.f);
+            tile_step<D, true>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, t1, P, W, l16, lg, !full,
+                               grp_b, 1.f, 1.f);
             if (!grp_b) __syncthreads();
             if (!have) break;
             cseg = nseg;
