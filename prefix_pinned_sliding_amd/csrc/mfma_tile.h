@@ -143,7 +143,7 @@ __device__ __forceinline__ void tile_qk(f32x4 (&s)[2][kTileKeys / 16], const Sof
 }
 
 template <int D>
-__device__ __forceinline__ void tile_max(f32x4 (&s)[2][kTileKeys / 16],
+__device__ __forceinline__ bool tile_max(f32x4 (&s)[2][kTileKeys / 16],
                                          SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
                                          int ct0, int t1, int P, int W, int lg, bool masked,
                                          float sc, float inv_sc) {
@@ -174,8 +174,9 @@ __device__ __forceinline__ void tile_max(f32x4 (&s)[2][kTileKeys / 16],
     }
     // The running max of a row only moves when some lane's own max exceeds it by the slack
     // (or the row has none yet); test that with one ballot, do the cross-lane max only then.
-    if (__any(ml[0] * sc + st.mb[0] > st.m[0] + kRescaleSlack ||
-              ml[1] * sc + st.mb[1] > st.m[1] + kRescaleSlack)) {
+    const bool moved = __any(ml[0] * sc + st.mb[0] > st.m[0] + kRescaleSlack ||
+                             ml[1] * sc + st.mb[1] > st.m[1] + kRescaleSlack);
+    if (moved) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const float mt = row_max4(ml[rb]) * sc + st.mb[rb];   // absolute tile max
@@ -193,6 +194,7 @@ __device__ __forceinline__ void tile_max(f32x4 (&s)[2][kTileKeys / 16],
             }
         }
     }
+    return moved;
 }
 
 template <int D>
@@ -238,14 +240,84 @@ __device__ __forceinline__ void tile_pv(SoftmaxRows<D / 16>& st, const bf16x8 (&
         }
 }
 
-// The exponentials and products of one tile, 32 keys at a time. The wave issues in order
-// (scheduling barriers fix it): the first step's V^T reads and exponentials, then the first
-// step's products with one exponential of the second step (and the second step's V^T
-// reads) between consecutive products, so that VALU work runs while the matrix core is
-// busy, then the second step's products.
+// P^T operands (bf16) of keys 32 h .. 32 h + 31 of the tile, from S^T.
+__device__ __forceinline__ void tile_exp_half(bf16x8 (&pb)[2], const f32x4 (&s)[2][kTileKeys / 16],
+                                              int h, float sc) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pb[rb][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * h][i] * sc);
+            pb[rb][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 * h + 1][i] * sc);
+        }
+}
+
+// S^T = K Q^T - mb as tile_qk computes it, keys 0-31 first, then keys 32-63 with the P^T
+// operands of keys 0-31 (`pb0`, exponentials against the running max from before this
+// tile) taken between those products. pb0 holds for the tile unless the tile is masked or
+// moves the running max (tile_max); the caller recomputes it then.
+template <int D>
+__device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x8 (&pb0)[2],
+                                            const SoftmaxRows<D / 16>& st,
+                                            const bf16x8 (&qop)[2][D / 32], const uint16_t* k_s,
+                                            int l16, int lg, float sc, float inv_sc) {
+    constexpr int KS = D / 32, KB = kTileKeys / 16;
+    constexpr int KSTR = D + kKPad;
+    static_assert(KB == 4 && 16 % KS == 0, "two halves of two 16-key blocks");
+    const float s0 = -st.mb[0] * inv_sc, s1 = -st.mb[1] * inv_sc;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        s[0][kb] = f32x4{s0, s0, s0, s0};
+        s[1][kb] = f32x4{s1, s1, s1, s1};
+    }
+    // steps (half h, k-step ks) in order; each reads the K operands of its two key blocks,
+    // one step ahead
+    constexpr int NS = 2 * KS;
+    bf16x8 ka[2][2];
+    const uint16_t* kp = k_s + l16 * KSTR + 8 * lg;
+    auto kread = [&](int step, int j) -> bf16x8 {
+        const int h = step / KS, ks = step % KS;
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(kp + (2 * h + j) * 16 * KSTR + ks * 32));
+    };
+    ka[0][0] = kread(0, 0);
+    ka[0][1] = kread(0, 1);
+#pragma unroll
+    for (int step = 0; step < NS; ++step) {
+        const int h = step / KS, ks = step % KS;
+        if (step + 1 < NS) {
+            ka[(step + 1) & 1][0] = kread(step + 1, 0);
+            ka[(step + 1) & 1][1] = kread(step + 1, 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kb = 2 * h + j;
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step & 1][j], qop[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step & 1][j], qop[1][ks], s[1][kb], 0, 0, 0);
+        }
+        if (h == 1) {
+            // 16 / KS of the 16 exponentials of keys 0-31 per step of the second half
+            constexpr int PER = 16 / KS;
+#pragma unroll
+            for (int e = PER * ks; e < PER * (ks + 1); ++e) {
+                const int rb = e / 8, i = e % 8;
+                pb0[rb][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][i / 4][i % 4] * sc);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // keeps the exponentials here: without it the compiler sinks them past the caller's
+    // branch that may recompute them
+    asm volatile("" : "+v"(pb0[0]), "+v"(pb0[1]));
+}
+
+// The products of one tile, 32 keys at a time, given the P^T operands of keys 0-31. The
+// wave issues in order (scheduling barriers fix it): keys 0-31's products with one
+// exponential of keys 32-63 (and their V^T reads) between consecutive products, so that
+// VALU work runs while the matrix core is busy, then keys 32-63's products.
 template <int D>
 __device__ __forceinline__ void tile_exp_pv(SoftmaxRows<D / 16>& st, const f32x4 (&s)[2][kTileKeys / 16],
-                                            const uint16_t* v_s, int l16, int lg, float sc) {
+                                            const bf16x8 (&pb0)[2], const uint16_t* v_s, int l16,
+                                            int lg, float sc) {
     constexpr int DB = D / 16, PVS = kTileKeys / 32;
     constexpr int VSTR = D + kVPad;
     static_assert(PVS == 2 && DB >= 4, "two 32-key steps per tile, at least 16 products each");
@@ -253,46 +325,41 @@ __device__ __forceinline__ void tile_exp_pv(SoftmaxRows<D / 16>& st, const f32x4
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
     const uint16_t* vrow = v_s + (4 * lg + l16 / 4) * VSTR + 4 * (l16 % 4);
     bf16x8 va[2][DB];
-    bf16x8 pb[2][PVS];
+    bf16x8 pb1[2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) va[0][db] = lds_read_tr2(vrow + db * 16, vrow + 16 * VSTR + db * 16);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pb[rb][0][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][0][i] * sc);
-            pb[rb][0][4 + i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][1][i] * sc);
-        }
     __builtin_amdgcn_sched_barrier(0);
-    st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][0], st.l[0], 0, 0, 0);
-    st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][0], st.l[1], 0, 0, 0);
-    // 16 exponentials of the second step over the first step's 2 DB products
+    st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb0[0], st.l[0], 0, 0, 0);
+    st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb0[1], st.l[1], 0, 0, 0);
+    // 16 exponentials of keys 32-63 over keys 0-31's 2 DB products
     constexpr int PER = 16 / DB;   // exponentials per db (two products)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][db], pb[0][0], st.o[0][db], 0, 0, 0);
-        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][db], pb[1][0], st.o[1][db], 0, 0, 0);
+        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][db], pb0[0], st.o[0][db], 0, 0, 0);
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][db], pb0[1], st.o[1][db], 0, 0, 0);
 #pragma unroll
         for (int e = db * PER; e < (db + 1) * PER; ++e) {
             const int rb = e / 8, i = e % 8;
-            pb[rb][1][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 + i / 4][i % 4] * sc);
+            pb1[rb][i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][2 + i / 4][i % 4] * sc);
         }
         va[1][db] = lds_read_tr2(vrow + 32 * VSTR + db * 16, vrow + 48 * VSTR + db * 16);
         __builtin_amdgcn_sched_barrier(0);
     }
-    st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][1], st.l[0], 0, 0, 0);
-    st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][1], st.l[1], 0, 0, 0);
+    st.l[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb1[0], st.l[0], 0, 0, 0);
+    st.l[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb1[1], st.l[1], 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][db], pb[0][1], st.o[0][db], 0, 0, 0);
-        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][db], pb[1][1], st.o[1][db], 0, 0, 0);
+        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][db], pb1[0], st.o[0][db], 0, 0, 0);
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][db], pb1[1], st.o[1][db], 0, 0, 0);
     }
 }
 
 // One whole tile: the three phases in order, with an optional workgroup barrier between
-// the products S^T and the softmax. With kSplitExp the exponentials and products run 32
-// keys at a time (tile_exp_pv); it pays where the products arrive in the log2 domain
-// (sc = 1): about 1% on the prefill kernel, and 3% slower on the training forward pass.
+// the products S^T and the softmax. With kSplitExp the tile runs 32 keys at a time: keys
+// 0-31's exponentials are taken during keys 32-63's S^T products (tile_qk_exp) and keys
+// 32-63's during keys 0-31's PV products (tile_exp_pv). It pays where the products arrive
+// in the log2 domain (sc = 1): about 1.5% on the prefill kernel; the training forward pass
+// ran 3% slower with it.
 template <int D, bool kSplitExp = false>
 __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
                                           const uint16_t* k_s, const uint16_t* v_s,
@@ -300,12 +367,16 @@ __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 
                                           int l16, int lg, bool masked, bool mid_barrier,
                                           float sc, float inv_sc) {
     f32x4 s[2][kTileKeys / 16];
-    tile_qk<D>(s, st, qop, k_s, l16, lg, inv_sc);
-    if (mid_barrier) __syncthreads();
     if constexpr (kSplitExp) {
-        tile_max<D>(s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
-        tile_exp_pv<D>(st, s, v_s, l16, lg, sc);
+        bf16x8 pb0[2];
+        tile_qk_exp<D>(s, pb0, st, qop, k_s, l16, lg, sc, inv_sc);
+        if (mid_barrier) __syncthreads();
+        if (tile_max<D>(s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc) || masked)
+            tile_exp_half(pb0, s, 0, sc);
+        tile_exp_pv<D>(st, s, pb0, v_s, l16, lg, sc);
     } else {
+        tile_qk<D>(s, st, qop, k_s, l16, lg, inv_sc);
+        if (mid_barrier) __syncthreads();
         bf16x8 pb[2][kTileKeys / 32];
         tile_softmax<D>(pb, s, st, row_pos, ct0, t1, P, W, lg, masked, sc, inv_sc);
         tile_pv<D>(st, pb, v_s, l16, lg);
