@@ -120,7 +120,7 @@ __device__ __forceinline__ void load_query(bf16x8 (&qo)[D / 32], const uint16_t*
 // The key ranges of a workgroup, in walk order: 0 = prefix in the cache, 1 = prefix
 // tokens inside the chunk (n < P), 2 = still-visible ring (n > P), 3 = window tokens of
 // the chunk. Prefix keys (ranges 0, 1) all come before window keys (2, 3). `win_lo` is
-// the first row's window start; walk_next steps (seg, t0) to the next tile some row sees.
+// the first row's window start; walk_next steps to the next tile [t0, t1) some row sees.
 struct Walk {
     int hi0, lo1, hi1, lo2, hi2, lo3, hi3, P, win_lo;
     __device__ int lo(int seg) const {
@@ -131,17 +131,39 @@ struct Walk {
     }
 };
 
+// Ranges 0, 1 and 3 are walked upwards from their start. Range 2 is walked downwards from
+// its end (the chunk's first position, the same for every workgroup of a sequence and KV
+// head) in tiles aligned to that end, so those workgroups, whose ring ranges differ only
+// in where they start, read each ring tile at about the same time and one L2 fill serves
+// them all; the partial tile is the lowest one.
 template <int BN>
-__device__ __forceinline__ bool walk_next(const Walk& w, int& seg, int& t0) {
+__device__ __forceinline__ bool walk_next(const Walk& w, int& seg, int& t0, int& t1) {
+    if (seg == 2) {
+        if (t0 > w.lo2) {
+            t1 = t0;
+            t0 = max(t1 - BN, w.lo2);
+            return true;
+        }
+        seg = 3;
+        t0 = w.lo3 - BN;
+    }
     t0 += BN;
     while (seg < 4) {
         const int hi = w.hi(seg);
         if (t0 >= hi) {
             ++seg;
+            if (seg == 2) {
+                if (w.hi2 > w.lo2) {
+                    t1 = w.hi2;
+                    t0 = max(t1 - BN, w.lo2);
+                    return true;
+                }
+                seg = 3;   // no ring keys
+            }
             if (seg < 4) t0 = w.lo(seg);
             continue;
         }
-        const int t1 = min(t0 + BN, hi);
+        t1 = min(t0 + BN, hi);
         // no row sees any key: all past the prefix and older than the first row's window
         if (t0 >= w.P && t1 - 1 < w.win_lo) {
             t0 += BN;
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
                       tab_s, c.Bs, c.bshift, c.n_blocks, pid >= 0};
 
     u32x4 kreg[KLD], vreg[KLD];
-    int seg = 0, t0 = -kBN;
+    int seg = 0, t0 = -kBN, t1 = 0;
     // Two groups of waves, A (waves 0 .. kPfWaves/2 - 1) and B (the rest), each SIMD holding
     // one wave of each. A passes the tile's barrier after its PV products, B after its QK^T
     // products, so on every SIMD one wave's softmax overlaps the other wave's products.
@@ -339,22 +361,22 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     // same for every wave of the workgroup, so all waves pass the same number of barriers:
     // one before the loop and one per tile.
     const bool grp_b = __builtin_amdgcn_readfirstlane(wave) >= kPfWaves / 2;
-    if (walk_next<kBN>(wk, seg, t0)) {
-        int cseg = seg, ct0 = t0, cur = 0;
-        fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+    if (walk_next<kBN>(wk, seg, t0, t1)) {
+        int cseg = seg, ct0 = t0, ct1 = t1, cur = 0;
+        fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
         stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
-        bool have = walk_next<kBN>(wk, seg, t0);
-        if (have) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+        bool have = walk_next<kBN>(wk, seg, t0, t1);
+        if (have) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
         __syncthreads();
 #pragma unroll 1
         while (true) {
-            const int nseg = seg, nt0 = t0;
+            const int nseg = seg, nt0 = t0, nt1 = t1;
             const int nxt = cur == 2 ? 0 : cur + 1;
             bool have_next = false;
             if (have) {
                 stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
-                have_next = walk_next<kBN>(wk, seg, t0);
-                if (have_next) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, wk.hi(seg), tid, kreg, vreg);
+                have_next = walk_next<kBN>(wk, seg, t0, t1);
+                if (have_next) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
             }
             if (q_prefix && cseg >= 2) {
 #pragma unroll
@@ -363,15 +385,15 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
                                   c.inv_freq, lg, q_sc);
                 q_prefix = false;
             }
-            const int t1 = min(ct0 + kBN, wk.hi(cseg));
-            const bool full = (ct0 + kBN == t1) && (t1 - 1 <= p_lo) &&
-                              (t1 - 1 < P || ct0 >= p_hi - W + 1);
-            tile_step<D, true>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, t1, P, W, l16, lg, !full,
+            const bool full = (ct0 + kBN == ct1) && (ct1 - 1 <= p_lo) &&
+                              (ct1 - 1 < P || ct0 >= p_hi - W + 1);
+            tile_step<D, true>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, ct1, P, W, l16, lg, !full,
                                grp_b, 1.f, 1.f);
             if (!grp_b) __syncthreads();
             if (!have) break;
             cseg = nseg;
             ct0 = nt0;
+            ct1 = nt1;
             have = have_next;
             cur = nxt;
         }
