@@ -265,6 +265,26 @@ __global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
     a.di[idx] = acc;
 }
 
+// Unpadded LDS tiles with the 16-byte chunk c of row r stored at chunk c ^ chunk_swz(r).
+// For rows r .. r + 7, chunk_swz is a permutation of 0 .. 7, so 16-byte row reads (8 lanes
+// on 8 consecutive rows, same logical chunk) fall in 8 different 16-byte bank groups; for
+// 4 consecutive rows chunk_swz / 2 is a permutation of 0 .. 3, so the 4 chunk pairs a
+// transposing read takes from 4 rows do too.
+__device__ __forceinline__ int chunk_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+// One wave-wide direct load into LDS: lane l's 16 bytes at `g` land at LDS byte address
+// lds + 16 l (global_load_lds_dwordx4, LDS base in M0). The compiler does not see this
+// load: the caller waits for it with lds_dma_wait (loads complete in issue order) and
+// publishes the data with a barrier.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const void* g) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void lds_dma_wait() {   // at most N vector-memory loads in flight
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------------------
 // dK, dV: one workgroup per (sequence, KV head, 64-key tile). Wave w owns keys
 // k0 + 16 w .. k0 + 16 w + 15. A query step is kBR rows = kBR / G positions x G heads.
@@ -272,11 +292,11 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int n_ktiles) {
     constexpr int BP = kBR / G;                 // positions per query step
     constexpr int KS = D / 32, DB = D / 16, RB = kBR / 16, RS = kBR / 32;
-    constexpr int QSTR = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t q_s[kBR * QSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t g_s[kBR * QSTR];
-    __shared__ __attribute__((aligned(16))) float lse_s[kBR];
-    __shared__ __attribute__((aligned(16))) float di_s[kBR];
+    // Q and dO tiles: two buffers each, unpadded rows with chunk_swz, filled by direct loads
+    __shared__ __attribute__((aligned(1024))) uint16_t q_s[2][kBR * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t g_s[2][kBR * D];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][kBR];
+    __shared__ __attribute__((aligned(16))) float di_s[2][kBR];
 
     const int total = n_ktiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
@@ -326,28 +346,55 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
     // query positions that see some key of the tile
     const int i_end = k0 < P ? len : min(len, k1 - 1 + W);
     const size_t row0 = (size_t)b * a.T * a.Hq + h * G;   // (row0 + i * Hq + g) * D
+    auto row_off = [&](int i0, int r) { return (row0 + (size_t)(i0 + r / G) * a.Hq + r % G) * D; };
+    // Step i0's Q and dO rows go straight from memory into buffer `buf` (each wave issues
+    // its share; the loads are waited for at the top of that step), its lse and D rows
+    // into registers; both one step ahead of the products.
+    const uint32_t q_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&q_s[0][0]));
+    const uint32_t g_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&g_s[0][0]));
+    float lse_r = 0.f, di_r = 0.f;
+    auto issue = [&](int i0, int buf) {
+        constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBR / RPL / kWaves;
+        static_assert(NPW * RPL * kWaves == kBR, "tile rows per wave");
+        const int last = (min(i0 + BP, len) - i0) * G - 1;
+#pragma unroll
+        for (int x = 0; x < NPW; ++x) {
+            const int blk = wave * NPW + x;
+            const int r = blk * RPL + lane / CPR;
+            const size_t e = row_off(i0, min(r, last)) + ((lane % CPR) ^ chunk_swz(r)) * 8;
+            const uint32_t o = (uint32_t)(buf * kBR * D * 2 + blk * 1024);
+            lds_dma16(q_lds + o, a.q + e);
+            lds_dma16(g_lds + o, a.dout + e);
+        }
+        if (tid < kBR) {
+            const size_t ri = row_off(i0, min(tid, last)) / D;
+            lse_r = a.lse[ri] * kLog2e;
+            di_r = a.di[ri];
+        }
+    };
+    // this lane's chunk swizzles: row reads (rows = l16 mod 8) and transposing reads
+    // (rows = 4 lg + l16 / 4 mod 8)
+    const int swz_row = chunk_swz(l16), swz_tr = chunk_swz(4 * lg + l16 / 4);
+    if (k0 < i_end) issue(k0, 0);
+    int buf = 0;
 #pragma unroll 1
-    for (int i0 = k0; i0 < i_end; i0 += BP) {
+    for (int i0 = k0; i0 < i_end; i0 += BP, buf ^= 1) {
         const int i1 = min(i0 + BP, len);             // positions [i0, i1)
         const int last = (i1 - i0) * G - 1;            // last valid row of the step
         const bool full = (i1 - i0 == BP) && (k1 - k0 == kBN) && (k1 - 1 <= i0) &&
                           (k1 - 1 < P || k0 >= (i1 - 1) - W + 1);
-        __syncthreads();
-        {
-            auto off = [&](int r) { return (row0 + (size_t)(i0 + r / G) * a.Hq + r % G) * D; };
-            RowTile<D, kBR> qr, gr;
-            qr.load(a.q, tid, last, off);
-            gr.load(a.dout, tid, last, off);
-            qr.template store<QSTR>(q_s, tid);
-            gr.template store<QSTR>(g_s, tid);
-        }
+        lds_dma_wait<0>();
         if (tid < kBR) {
-            const int r = min(tid, last);
-            const size_t ri = row0 + (size_t)(i0 + r / G) * a.Hq + r % G;
-            lse_s[tid] = a.lse[ri] * kLog2e;
-            di_s[tid] = a.di[ri];
+            lse_s[buf][tid] = lse_r;
+            di_s[buf][tid] = di_r;
         }
+        // step i0's tiles are in place, and every wave is done with the other buffer
         __syncthreads();
+        if (i0 + BP < i_end) issue(i0 + BP, buf ^ 1);
+        const uint16_t* qt = q_s[buf];
+        const uint16_t* gt = g_s[buf];
 
         // S = Q K^T and dP = dO V^T for this wave's 16 keys; lane: rows 16 rb + 4 lg + i
         f32x4 s[RB], dp[RB];
@@ -357,9 +404,9 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
             dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int e = (rb * 16 + l16) * QSTR + ks * 32 + 8 * lg;
-                const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(q_s + e));
-                const bf16x8 ga = as_bf16x8(*reinterpret_cast<const u32x4*>(g_s + e));
+                const int e = (rb * 16 + l16) * D + ((ks * 4 + lg) ^ swz_row) * 8;
+                const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + e));
+                const bf16x8 ga = as_bf16x8(*reinterpret_cast<const u32x4*>(gt + e));
                 s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[ks], s[rb], 0, 0, 0);
                 dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vop[ks], dp[rb], 0, 0, 0);
             }
@@ -368,8 +415,8 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         bf16x8 pa[RS], sa[RS];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float4 ls = *reinterpret_cast<const float4*>(lse_s + rb * 16 + 4 * lg);
-            const float4 ds = *reinterpret_cast<const float4*>(di_s + rb * 16 + 4 * lg);
+            const float4 ls = *reinterpret_cast<const float4*>(&lse_s[buf][rb * 16 + 4 * lg]);
+            const float4 ds = *reinterpret_cast<const float4*>(&di_s[buf][rb * 16 + 4 * lg]);
             const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -387,8 +434,10 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int rs = 0; rs < RS; ++rs) {
-                const bf16x8 gb = tr_operand<QSTR>(g_s, rs, db * 16, l16, lg);
-                const bf16x8 qb = tr_operand<QSTR>(q_s, rs, db * 16, l16, lg);
+                const int e = (32 * rs + 4 * lg + l16 / 4) * D +
+                              ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
+                const bf16x8 gb = lds_read_tr2(gt + e, gt + e + 16 * D);
+                const bf16x8 qb = lds_read_tr2(qt + e, qt + e + 16 * D);
                 dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rs], gb, dv[db], 0, 0, 0);
                 dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[rs], qb, dk[db], 0, 0, 0);
             }
