@@ -69,42 +69,6 @@ struct KeyWalk {
     }
 };
 
-// Row-major copy of a ROWS x D tile through registers: consecutive lanes take consecutive
-// 16-byte chunks of a row (conflict-free LDS stores); row r comes from src + off(r) (element
-// offset), rows beyond `last` repeat row `last`. Transposed operands are read back from the
-// row-major copy with ds_read_b64_tr_b16 (lds_read_tr2).
-template <int D, int ROWS>
-struct RowTile {
-    static constexpr int CPR = D / 8;
-    static constexpr int N = ROWS * CPR / kBlock;
-    u32x4 r[N];
-    template <typename Off>
-    __device__ __forceinline__ void load(const uint16_t* src, int tid, int last, Off off) {
-#pragma unroll
-        for (int x = 0; x < N; ++x) {
-            const int ci = tid + kBlock * x;
-            r[x] = *reinterpret_cast<const u32x4*>(src + off(min(ci / CPR, last)) + (ci % CPR) * 8);
-        }
-    }
-    template <int STR>
-    __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
-#pragma unroll
-        for (int x = 0; x < N; ++x) {
-            const int ci = tid + kBlock * x;
-            *reinterpret_cast<u32x4*>(dst + (ci / CPR) * STR + (ci % CPR) * 8) = r[x];
-        }
-    }
-};
-
-// The transposed operand for rows 32 s + 4 lg + j (slots 0..3) and 32 s + 16 + 4 lg + j
-// (slots 4..7), column c0 + l16, of a row-major tile with row stride STR: the k order of
-// an accumulator pair (rows 0..15 and 16..31 of a 32-row group).
-template <int STR>
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int s32, int c0, int l16, int lg) {
-    const uint16_t* p = tile + (32 * s32 + 4 * lg + l16 / 4) * STR + c0 + 4 * (l16 % 4);
-    return lds_read_tr2(p, p + 16 * STR);
-}
-
 // ---------------------------------------------------------------------------------------
 // Forward: the chunked-prefill kernel's schedule on row-space tiles. 8 waves, 256 rows per
 // workgroup in two groups of 4 waves running half a tile apart (group A passes the tile's
@@ -463,9 +427,9 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_qtiles) {
     constexpr int BQ = kRows / G;
     constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    constexpr int KSTR = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t v_s[kBN * KSTR];
+    // K and V tiles: two buffers each, unpadded rows with chunk_swz, filled by direct loads
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s[2][kBN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s[2][kBN * D];
 
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
@@ -511,21 +475,46 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
 
     const KeyWalk wk{min(P, p_hi + 1), max(P, p_lo - W + 1), p_hi + 1};
     const size_t kv0 = (size_t)b * a.T * a.Hkv + h;
-    int seg = 0, t0 = -kBN;
+    // The next key tile's K and V rows go straight from memory into the other buffer
+    // while this one is used (each wave issues its share; waited for at the top of the tile).
+    const uint32_t k_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&k_s[0][0]));
+    const uint32_t v_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&v_s[0][0]));
+    auto issue = [&](int sg, int s0, int buf) {
+        constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBN / RPL / kWaves;
+        static_assert(NPW * RPL * kWaves == kBN, "tile rows per wave");
+        const int last = min(s0 + kBN, sg == 0 ? wk.hi0 : wk.hi1) - 1 - s0;
+#pragma unroll
+        for (int x = 0; x < NPW; ++x) {
+            const int blk = wave * NPW + x;
+            const int r = blk * RPL + lane / CPR;
+            const size_t e = (kv0 + (size_t)(s0 + min(r, last)) * a.Hkv) * D +
+                             ((lane % CPR) ^ chunk_swz(r)) * 8;
+            const uint32_t o = (uint32_t)(buf * kBN * D * 2 + blk * 1024);
+            lds_dma16(k_lds + o, a.k + e);
+            lds_dma16(v_lds + o, a.v + e);
+        }
+    };
+    // this lane's chunk swizzles: row reads (rows = l16 mod 8) and transposing reads
+    // (rows = 4 lg + l16 / 4 mod 8)
+    const int swz_row = chunk_swz(l16), swz_tr = chunk_swz(4 * lg + l16 / 4);
+    int seg = 0, t0 = -kBN, buf = 0;
+    bool have = wk.next(seg, t0);
+    if (have) issue(seg, t0, 0);
 #pragma unroll 1
-    while (wk.next(seg, t0)) {
+    while (have) {
         const int t1 = min(t0 + kBN, seg == 0 ? wk.hi0 : wk.hi1);
         const bool full = (t0 + kBN == t1) && (t1 - 1 <= p_lo) && (t1 - 1 < P || t0 >= p_hi - W + 1);
+        const int ct0 = t0;
+        lds_dma_wait<0>();
+        // this tile is in place, and every wave is done with the other buffer
         __syncthreads();
-        {
-            auto off = [&](int r) { return (kv0 + (size_t)(t0 + r) * a.Hkv) * D; };
-            RowTile<D, kBN> kr, vr;
-            kr.load(a.k, tid, t1 - 1 - t0, off);
-            vr.load(a.v, tid, t1 - 1 - t0, off);
-            kr.template store<KSTR>(k_s, tid);
-            vr.template store<KSTR>(v_s, tid);
-        }
-        __syncthreads();
+        have = wk.next(seg, t0);
+        if (have) issue(seg, t0, buf ^ 1);
+        const uint16_t* kt = k_s[buf];
+        const uint16_t* vt = v_s[buf];
+        buf ^= 1;
 
         // S^T = K Q^T, dP^T = V dO^T; lane: keys 16 kb + 4 lg + i, row l16
         f32x4 s[2][KB], dp[2][KB];
@@ -538,9 +527,9 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int e = (kb * 16 + l16) * KSTR + ks * 32 + 8 * lg;
-                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(k_s + e));
-                const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(v_s + e));
+                const int e = (kb * 16 + l16) * D + ((ks * 4 + lg) ^ swz_row) * 8;
+                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + e));
+                const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + e));
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[rb][ks], s[rb][kb], 0, 0, 0);
@@ -556,7 +545,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int j = t0 + kb * 16 + 4 * lg + i;
+                    const int j = ct0 + kb * 16 + 4 * lg + i;
                     const bool vis = full || (j < t1 && visible(row_pos[rb], j, P, W));
                     const float p = vis ? __builtin_amdgcn_exp2f(s[rb][kb][i] * sc - lse2[rb]) : 0.f;
                     sb[rb][kb / 2][(kb & 1) * 4 + i] = (__bf16)(p * (dp[rb][kb][i] - di[rb]));
@@ -566,7 +555,9 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int ps = 0; ps < PVS; ++ps) {
-                const bf16x8 ka = tr_operand<KSTR>(k_s, ps, db * 16, l16, lg);
+                const int e = (32 * ps + 4 * lg + l16 / 4) * D +
+                              ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
+                const bf16x8 ka = lds_read_tr2(kt + e, kt + e + 16 * D);
                 acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[0][ps], acc[0][db], 0, 0, 0);
                 acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[1][ps], acc[1][db], 0, 0, 0);
             }
