@@ -375,35 +375,51 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
                 dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vop[ks], dp[rb], 0, 0, 0);
             }
         }
-        // P and dS as A operands of the row contraction (k = rows, order of vt_col)
+        // P and dS as A operands of the row contraction (k = rows, order of vt_col). The
+        // products of rows 0-31 (rs = 0) are issued with the P and dS values of rows 32-63
+        // computed between them (scheduling barriers fix the order), so the wave's VALU work
+        // runs while the matrix core is busy.
+        static_assert(RS == 2 && RB == 4, "two 32-row halves per step");
         bf16x8 pa[RS], sa[RS];
+        float4 lsq[RB], dsq[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float4 ls = *reinterpret_cast<const float4*>(&lse_s[buf][rb * 16 + 4 * lg]);
-            const float4 ds = *reinterpret_cast<const float4*>(&di_s[buf][rb * 16 + 4 * lg]);
-            const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = rb * 16 + 4 * lg + i;
-                const bool vis = full || (r <= last && key < k1 &&
-                                          visible(i0 + r / G, key, P, W));
-                const float p = vis ? __builtin_amdgcn_exp2f(s[rb][i] * sc - lsv[i]) : 0.f;
-                const float d = p * (dp[rb][i] - dsv[i]);
-                pa[rb / 2][(rb & 1) * 4 + i] = (__bf16)p;
-                sa[rb / 2][(rb & 1) * 4 + i] = (__bf16)d;
-            }
+            lsq[rb] = *reinterpret_cast<const float4*>(&lse_s[buf][rb * 16 + 4 * lg]);
+            dsq[rb] = *reinterpret_cast<const float4*>(&di_s[buf][rb * 16 + 4 * lg]);
         }
+        auto pds = [&](int rb, int i) {   // P and dS of row 16 rb + 4 lg + i
+            const float ls = i == 0 ? lsq[rb].x : (i == 1 ? lsq[rb].y : (i == 2 ? lsq[rb].z : lsq[rb].w));
+            const float ds = i == 0 ? dsq[rb].x : (i == 1 ? dsq[rb].y : (i == 2 ? dsq[rb].z : dsq[rb].w));
+            const int r = rb * 16 + 4 * lg + i;
+            const bool vis = full || (r <= last && key < k1 && visible(i0 + r / G, key, P, W));
+            const float p = vis ? __builtin_amdgcn_exp2f(s[rb][i] * sc - ls) : 0.f;
+            const float d = p * (dp[rb][i] - ds);
+            pa[rb / 2][(rb & 1) * 4 + i] = (__bf16)p;
+            sa[rb / 2][(rb & 1) * 4 + i] = (__bf16)d;
+        };
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pds(rb, i);
+        __builtin_amdgcn_sched_barrier(0);
         // dV += P^T dO, dK += dS^T Q (scaled at the end)
+        constexpr int PER = 8 / DB;   // values of rows 32-63 per d-block of rows 0-31
+        static_assert(PER * DB == 8, "d-blocks per step");
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
-            for (int rs = 0; rs < RS; ++rs) {
+            for (int db = 0; db < DB; ++db) {
                 const int e = (32 * rs + 4 * lg + l16 / 4) * D +
                               ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
                 const bf16x8 gb = lds_read_tr2(gt + e, gt + e + 16 * D);
                 const bf16x8 qb = lds_read_tr2(qt + e, qt + e + 16 * D);
                 dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rs], gb, dv[db], 0, 0, 0);
                 dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[rs], qb, dk[db], 0, 0, 0);
+                if (rs == 0) {
+#pragma unroll
+                    for (int x = db * PER; x < (db + 1) * PER; ++x) pds(2 + x / 4, x % 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
     }
 
