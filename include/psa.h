@@ -73,14 +73,16 @@ enum { PSA_BF16 = 0, PSA_F32 = 1 };
 
 /* Cache description. */
 typedef struct {
-    int32_t max_batch;   /* number of sequences B >= 1 */
+    int32_t max_batch;   /* number of sequences B, 1 <= B <= 65535 */
     int32_t n_q_heads;   /* H_q >= 1, a multiple of n_kv_heads, H_q / H_kv in {1, 2, 4, 8} */
-    int32_t n_kv_heads;  /* H_kv >= 1 */
+    int32_t n_kv_heads;  /* H_kv, 1 <= H_kv <= 65535 */
     int32_t head_dim;    /* D: 64 or 128 */
     int32_t prefix_max;  /* P_max >= 0: largest pinned-prefix length any sequence may use */
-    int32_t window;      /* W >= 1: window length (the largest psa_seq_set_window accepts) */
+    int32_t window;      /* W >= 1: window length (the largest psa_seq_set_window accepts);
+                            prefix_max + window <= 2^30, and W < 2^24 when max_chunk > 0 */
     int32_t dtype;       /* PSA_BF16 or PSA_F32 (storage, inputs and outputs) */
-    int32_t max_chunk;   /* largest prefill chunk C (0: psa_prefill_attn unavailable) */
+    int32_t max_chunk;   /* largest prefill chunk C (0: psa_prefill_attn unavailable);
+                            C * n_kv_heads * head_dim < 2^32 */
     double rope_base;    /* > 0, e.g. 10000 */
     float scale;         /* softmax scale; 0 selects 1 / sqrt(head_dim) */
     int32_t n_shared_prefixes; /* >= 0: entries of the shared-prefix pool */
@@ -140,6 +142,9 @@ typedef struct {
     int32_t elem_bytes;   /* 2 (bf16) or 4 (f32) */
     int32_t block_size;   /* 0 (contiguous) or the block size */
     int32_t n_blocks;     /* paged: physical blocks in the pool */
+    int32_t max_splits;   /* decode splits the workspace holds per (sequence, query head):
+                             enough for max(prefix_max, shared_prefix_max) + window visible
+                             entries at the shortest split (128 entries) */
 } psa_layout;
 
 /* Device bytes the caller must provide for a cache described by *desc (0 if *desc is
@@ -240,7 +245,9 @@ int psa_append(psa_cache *cache, const int32_t *n_new_host, int32_t n_uniform, c
  * window blocks are read). The query of sequence b is the token at p = len_b - 1,
  * i.e. the one most recently appended; it sees the prefix and the window, itself
  * included. q, out: [B][H_q][D]; lse: [B][H_q] float32 natural-log log-sum-exp of the
- * scaled logits, or NULL. Errors: PSA_ERR_STATE if any sequence is empty. */
+ * scaled logits, or NULL. Errors: PSA_ERR_STATE if any sequence is empty, or if the split
+ * plan needs more than psa_layout.max_splits splits (refused before any launch; the layout's
+ * sizing rules it out). */
 int psa_decode_attn(psa_cache *cache, const void *q, void *out, float *lse, psa_stream stream);
 
 /* One step of the generation loop ([PS] 03: append the new token, then attend to the
@@ -250,7 +257,9 @@ int psa_decode_attn(psa_cache *cache, const void *q, void *out, float *lse, psa_
  * n_stride = 1); q, out, lse as psa_decode_attn. Errors: PSA_ERR_ARG for a NULL k, v,
  * q or out; PSA_ERR_STATE if a sequence was never reset or (paged) the pool has no free
  * block for a token that needs one; PSA_ERR_OVERFLOW as psa_append. These leave the
- * cache unchanged; PSA_ERR_HIP (a failed launch) may leave it advanced by the step. */
+ * cache unchanged. PSA_ERR_HIP: a failed decode launch leaves the cache unchanged (paged:
+ * the blocks the token needed stay mapped); a failed merge launch leaves it advanced by the
+ * step, with `out` and `lse` not written. */
 int psa_decode_step(psa_cache *cache, const void *k, const void *v, const void *q, void *out,
                     float *lse, psa_stream stream);
 

@@ -167,18 +167,6 @@ def attend_view(q: np.ndarray, p: int, hist: History, view, n_kv_heads: int, bas
     return out, lse
 
 
-def decode_batch(q: np.ndarray, positions, hists, prefixes, W: int, n_kv_heads: int,
-                 base: float, scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """decode_query for every sequence: q[B, H_q, D], positions[B], hists[B], prefixes[B]."""
-    outs, lses = [], []
-    for b in range(q.shape[0]):
-        o, s = decode_query(q[b], int(positions[b]), hists[b], int(prefixes[b]), W,
-                            n_kv_heads, base, scale)
-        outs.append(o)
-        lses.append(s)
-    return np.stack(outs), np.stack(lses)
-
-
 def prefill_chunk(q: np.ndarray, n: int, hist: History, P: int, W: int, n_kv_heads: int,
                   base: float, scale: float, rows=None, pe: str = "continue"
                   ) -> Tuple[np.ndarray, np.ndarray]:

@@ -64,6 +64,7 @@ class Layout(ctypes.Structure):
         ("elem_bytes", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("n_blocks", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
     ]
 
 

@@ -65,8 +65,10 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
         *why = w;
         return false;
     };
-    if (d.max_batch < 1) return bad("max_batch must be >= 1");
-    if (d.n_kv_heads < 1) return bad("n_kv_heads must be >= 1");
+    // The decode launch puts sequences on grid z and KV heads on grid y, the merge launch
+    // sequences on grid y: both dimensions hold at most 65535.
+    if (d.max_batch < 1 || d.max_batch > kMaxGridYZ) return bad("max_batch must be in [1, 65535]");
+    if (d.n_kv_heads < 1 || d.n_kv_heads > kMaxGridYZ) return bad("n_kv_heads must be in [1, 65535]");
     if (d.n_q_heads < 1 || d.n_q_heads % d.n_kv_heads != 0)
         return bad("n_q_heads must be a positive multiple of n_kv_heads");
     const int G = d.n_q_heads / d.n_kv_heads;
@@ -87,6 +89,14 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
         return bad("pe_mode must be PSA_PE_CONTINUE or PSA_PE_RESET");
     const int64_t S = (int64_t)d.prefix_max + d.window;
     if (S > (1 << 30)) return bad("prefix_max + window too large");
+    // Chunked prefill addresses a tile's K/V rows as 24-bit row x 24-bit stride products
+    // with a 32-bit result (elements): ring rows (< W) times D, and chunk rows (< chunk)
+    // times H_kv * D.
+    if (d.max_chunk > 0) {
+        if (d.window >= (1 << 24)) return bad("window must be < 2^24 when max_chunk > 0");
+        if ((int64_t)d.max_chunk * d.n_kv_heads * d.head_dim >= ((int64_t)1 << 32))
+            return bad("max_chunk * n_kv_heads * head_dim must be < 2^32");
+    }
     int64_t n_blocks = 0;
     if (d.block_size != 0) {
         const int bs = d.block_size;
@@ -103,8 +113,11 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     const size_t elem = d.dtype == PSA_BF16 ? 2 : 4;
     const size_t B = (size_t)d.max_batch, Hq = (size_t)d.n_q_heads, Hkv = (size_t)d.n_kv_heads;
     const size_t D = (size_t)d.head_dim;
-    // RESET splits the prefix and the window separately: one more split at most.
-    const int64_t max_splits = (S + kSplitGranule - 1) / kSplitGranule + 1;
+    // A sequence sees at most max(prefix_max, shared_prefix_max) + window entries (an
+    // attached sequence's prefix is its pool entry). Splits hold at least kSplitGranule
+    // entries; RESET splits the prefix and the window separately: one more split at most.
+    const int64_t seen = (int64_t)std::max(d.prefix_max, d.shared_prefix_max) + d.window;
+    const int64_t max_splits = (seen + kSplitGranule - 1) / kSplitGranule + 1;
     const size_t A = 256;
     size_t off = 0;
     const size_t kv_rows = d.block_size ? (size_t)n_blocks * Hkv * (size_t)d.block_size
@@ -237,6 +250,27 @@ int auto_split_tokens(psa_cache* c) {
 }
 
 bool valid_seq(const psa_cache* c, int32_t seq) { return seq >= 0 && seq < c->desc.max_batch; }
+
+// Split length and the largest split count over the batch for a decode of the current host
+// state. Every split's partial result has a slot in the workspace ([B][Hq][max_splits]);
+// a plan that needs more is refused before anything is enqueued (the layout sizes
+// max_splits for the longest visible list at the smallest split length, so this holds
+// unless the sizing is wrong).
+int plan_decode(psa_cache* c, int* split_len, int* grid_splits) {
+    const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
+    int64_t max_ns = 1;
+    for (int b = 0; b < c->desc.max_batch; ++b) {
+        const psa::SeqView v = view_of(c, b);
+        const int64_t ns = psa::split_count(v.n_pre, v.n_win, L, c->desc.pe_mode);
+        if (ns > max_ns) max_ns = ns;
+    }
+    if (max_ns > c->L.max_splits)
+        return fail(PSA_ERR_STATE, "decode needs " + std::to_string(max_ns) + " splits, the workspace holds " +
+                                       std::to_string(c->L.max_splits));
+    *split_len = L;
+    *grid_splits = (int)max_ns;
+    return PSA_OK;
+}
 
 // Decode workgroups go out sequence by sequence in the device order array (grid z); with
 // sequences of different lengths, the longest first, so the short ones fill the end of
@@ -418,6 +452,7 @@ PSA_API int psa_cache_layout(const psa_cache_desc* desc, psa_layout* out) {
     out->btab_offset = L.btab;
     out->block_size = desc->block_size;
     out->n_blocks = L.n_blocks;
+    out->max_splits = L.max_splits;
     return PSA_OK;
 }
 
@@ -705,19 +740,15 @@ PSA_API int psa_decode_attn(psa_cache* c, const void* q, void* out, float* lse, 
         if (c->pre[b] < 0) return fail(PSA_ERR_STATE, "decode on a sequence that was never reset");
         if (c->len[b] < 1) return fail(PSA_ERR_STATE, "decode on an empty sequence");
     }
-    const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
-    int64_t max_ns = 1;
-    for (int b = 0; b < B; ++b) {
-        const psa::SeqView v = view_of(c, b);
-        const int64_t ns = psa::split_count(v.n_pre, v.n_win, L, c->desc.pe_mode);
-        if (ns > max_ns) max_ns = ns;
-    }
+    int L = 0, max_ns = 0;
+    const int prc = plan_decode(c, &L, &max_ns);
+    if (prc != PSA_OK) return prc;
     hipStream_t s = (hipStream_t)stream;
     const int orc = update_decode_order(c, s);
     if (orc != PSA_OK) return orc;
     const int cur = c->cur;
     int rc = timed(c, PSA_K_DECODE, s, "decode partial", [&] {
-        return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, nullptr, nullptr, s);
+        return psa::launch_decode_partial(c->dev, q, L, max_ns, cur, nullptr, nullptr, s);
     });
     if (rc != PSA_OK) return rc;
     return timed(c, PSA_K_MERGE, s, "split merge",
@@ -735,25 +766,34 @@ PSA_API int psa_decode_step(psa_cache* c, const void* k, const void* v, const vo
         if (c->len[b] + 1 > INT32_MAX) return fail(PSA_ERR_OVERFLOW, "sequence length overflow");
     }
     hipStream_t s = (hipStream_t)stream;
+    // Split planning and the decode order see the state after the append, as
+    // psa_decode_attn would; the host lengths keep it only if every launch succeeds.
+    auto undo = [&] {
+        for (int b = 0; b < B; ++b) c->len[b] -= 1;
+    };
+    for (int b = 0; b < B; ++b) c->len[b] += 1;
+    int L = 0, max_ns = 0;
+    const int prc = plan_decode(c, &L, &max_ns);
+    if (prc != PSA_OK) {
+        undo();
+        return prc;
+    }
+    for (int b = 0; b < B; ++b) c->len[b] -= 1;
     const int mrc = map_append(c, nullptr, 1, s);
     if (mrc != PSA_OK) return mrc;
-    // Split planning sees the state after the append, as psa_decode_attn would.
     for (int b = 0; b < B; ++b) c->len[b] += 1;
-    const int L = c->split_tokens > 0 ? c->split_tokens : auto_split_tokens(c);
-    int64_t max_ns = 1;
-    for (int b = 0; b < B; ++b) {
-        const psa::SeqView sv = view_of(c, b);
-        const int64_t ns = psa::split_count(sv.n_pre, sv.n_win, L, c->desc.pe_mode);
-        if (ns > max_ns) max_ns = ns;
-    }
-    const int orc = update_decode_order(c, s);
-    if (orc != PSA_OK) return orc;
+    int rc = update_decode_order(c, s);
     const int cur = c->cur;
+    if (rc == PSA_OK)
+        rc = timed(c, PSA_K_DECODE, s, "decode step", [&] {
+            return psa::launch_decode_partial(c->dev, q, L, max_ns, cur, k, v, s);
+        });
+    if (rc != PSA_OK) {
+        undo();
+        return rc;
+    }
+    // The decode launch appended the token on the device: the step has happened.
     c->cur ^= 1;
-    int rc = timed(c, PSA_K_DECODE, s, "decode step", [&] {
-        return psa::launch_decode_partial(c->dev, q, L, (int)max_ns, cur, k, v, s);
-    });
-    if (rc != PSA_OK) return rc;
     return timed(c, PSA_K_MERGE, s, "split merge",
                  [&] { return psa::launch_merge(c->dev, out, lse, L, cur ^ 1, s); });
 }

@@ -11,6 +11,7 @@ namespace psa {
 
 constexpr int kSplitGranule = 128;   // decode split lengths are multiples of this
 constexpr int kMaxGroup = 8;         // largest supported H_q / H_kv
+constexpr int kMaxGridYZ = 65535;    // largest grid y / z dimension the launches use
 
 // Device view of one cache: base pointers carved out of the caller's buffer.
 struct DevCache {

@@ -85,6 +85,38 @@ def test_invalid_rope_base_scale_dtype(psa):
         assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0, field
 
 
+@pytest.mark.parametrize("bad", [
+    dict(max_batch=65536), dict(n_q_heads=65536 * 2, n_kv_heads=65536),
+    dict(window=1 << 24),                                        # prefill ring rows need < 2^24
+    dict(max_chunk=(1 << 32) // (8 * 128)),                      # chunk rows x H_kv x D >= 2^32
+])
+def test_shapes_beyond_the_kernels_addressing_are_rejected(psa, bad):
+    d = good_desc(psa, prefix_max=0, **bad)
+    assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0, bad
+    assert psa.lib.psa_last_error().decode() != ""
+
+
+def test_long_window_is_accepted_without_prefill(psa):
+    # the 24-bit row bound belongs to chunked prefill only
+    d = good_desc(psa, max_batch=1, n_q_heads=8, n_kv_heads=8, prefix_max=0, window=1 << 24,
+                  max_chunk=0)
+    assert psa.cache_layout(d).slots == 1 << 24
+    assert psa.cache_layout(good_desc(psa, max_chunk=(1 << 32) // (8 * 128) - 1)).slots == 4196
+
+
+def test_split_slots_cover_shared_prefixes(psa):
+    # an attached sequence sees up to shared_prefix_max + window entries, more than
+    # prefix_max + window: the decode workspace must hold the splits of that many
+    d = good_desc(psa, prefix_max=0, window=128, n_shared_prefixes=1, shared_prefix_max=512,
+                  max_chunk=0)
+    L = psa.cache_layout(d)
+    assert L.max_splits >= -(-(512 + 128) // 128)          # 5 splits of 128 entries
+    assert psa.cache_layout(good_desc(psa)).max_splits >= -(-(100 + 4096) // 128)
+    # RESET cuts the prefix and the window separately: one more split
+    r = psa.cache_layout(good_desc(psa, pe="reset"))
+    assert r.max_splits >= -(-100 // 128) + -(-4096 // 128)
+
+
 def test_paged_layout(psa):
     # K/V become a pool of blocks [H_kv][n_blocks][Bs][D]; the block table follows the tags
     d = good_desc(psa, prefix_max=128, block_size=64)

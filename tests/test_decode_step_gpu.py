@@ -188,7 +188,8 @@ def test_errors_leave_the_state_unchanged():
 
 def test_default_workload_full_size():
     # the default decode workload (64 sequences at t = 32768, P = 100, W = 4096): several
-    # fused steps, outputs equal to the two-call path, sampled sequences against the oracle
+    # fused steps, outputs equal to the two-call path bit for bit (their parity with the
+    # oracle over the whole tensor is test_full_size_gpu.py's)
     wl = configs.decode_p100_w4096()
     n0 = [t - 1 for t in wl.start]
     caches = [drive.make_cache(wl) for _ in range(2)]
@@ -204,9 +205,4 @@ def test_default_workload_full_size():
         of = fused.decode_step(k[:, 0].contiguous(), v[:, 0].contiguous(), q)
         assert torch.equal(ot, of), f"step {step}"
         n = [x + 1 for x in n]
-    out = of.double().cpu().numpy()
-    qc = q.double().cpu().numpy()
-    for s in [0, 21, 63]:
-        ref, _ = attn.decode_query(qc[s], n[s] - 1, drive.hist_provider(wl, s), wl.prefix[s],
-                                   wl.window, wl.n_kv_heads, wl.rope_base, wl.scale)
-        tol_check(out[s], ref, wl.dtype, f"seq {s}")
+    same_state(two, fused, wl.batch)

@@ -1,0 +1,179 @@
+"""Whole-tensor parity at full size: every sequence, every row, every step of the decode and
+prefill workloads, against the float64 oracle run on a pool of host processes.
+
+Criteria (per call, over the whole output tensor [B][H_q][D] or [B][C][H_q][D]):
+max |out - ref| <= 2e-2 and ||out - ref||_2 / ||ref||_2 <= 5e-3 for bfloat16 storage; lse
+within 2e-2 (the bound derived in test_decode_gpu.py: the oracle rotates keys without
+rounding, the cache holds them rounded once). The worst call is printed.
+
+The cache after the run is exported for every sequence and compared bit for bit with the
+list model's expected view ([KV-Lean] 6.3: export the structure and compare it with the
+specification): positions, stored key bits (rotated at the absolute position in float64 and
+rounded once), value bits. The comparison is of SHA-256 digests of the three arrays; on a
+mismatch the sequence's arrays are compared element by element for the report.
+
+The workloads are the synthetic stand-ins for the pages' reasoning traces: decode at
+t = 32768 with P = 100, W = 4096 (64 sequences); t = 100000 with P = 512, W = 16384 (32
+sequences, 32/8 heads); a 512-token chunk per sequence at t ~ U{8192..65536} (8 sequences);
+256 sequences with P_b ~ U{50..2000} and log-uniform t_b in [1000, 131072] over 64 steps.
+The decode calls are the ones the benchmark times (the fused step, automatic splits),
+alternating with the two-call path where a workload runs several steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle_pool as op
+from synth import configs, drive
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2, LSE_ATOL = 2e-2, 5e-3, 2e-2
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_call(out: np.ndarray, ref: np.ndarray, lse=None, ref_lse=None, what=""):
+    err, rel = op.whole_tensor_error(out, ref)
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    assert err <= MAX_ABS and rel <= REL_L2, f"{what}: max-abs {err:.3e} rel-l2 {rel:.3e}"
+    if lse is not None:
+        lerr = float(np.abs(lse - ref_lse).max())
+        assert lerr <= LSE_ATOL, f"{what}: lse max-abs {lerr:.3e}"
+    return err, rel
+
+
+def check_exports(c, wl, n_final, what):
+    """Every sequence's exported cache against the list model, bit for bit."""
+    want = op.run(op.expected_view_job, [(wl, b, n_final[b], "bf16") for b in range(wl.batch)])
+    bad = []
+    for b in range(wl.batch):
+        k_e, v_e, pos_e = c.export(b)
+        got = (len(pos_e), op.view_digest(pos_e.numpy(), bits(k_e), bits(v_e)))
+        if got != want[b]:
+            bad.append(b)
+    if bad:
+        from oracle import cache as ocache
+        b = bad[0]
+        k_e, v_e, pos_e = c.export(b)
+        pos, kbits, vref = ocache.expected_view(wl.prefix[b], wl.window_of(b), n_final[b],
+                                                drive.hist_provider(wl, b), wl.rope_base, "bf16")
+        detail = f"count {len(pos_e)} vs {len(pos)}"
+        if len(pos) == len(pos_e):
+            detail += (f", positions differ at {int((pos_e.numpy() != pos).sum())}, key bits at "
+                       f"{int((bits(k_e) != kbits).sum())}, values at "
+                       f"{int((v_e.double().numpy() != vref).sum())} elements")
+        pytest.fail(f"{what}: {len(bad)} sequences differ from the list model (first {b}: {detail})")
+    print(f"{what}: {wl.batch} exported caches bit-exact")
+
+
+def decode_steps(wl, steps: int, fused_every: int = 1):
+    """Fill to t_b - 1, then `steps` decode steps (fused when step % fused_every == 0, else
+    append + decode); every output of every step against the oracle."""
+    B = wl.batch
+    n0 = [t - 1 for t in wl.start]
+    pos = np.array([[n + s for s in range(steps)] for n in n0])            # [B][steps]
+    q_cpu = [drive.queries(wl, list(pos[:, s]), "cpu") for s in range(steps)]
+    qd = [q.double().numpy() for q in q_cpu]
+    jobs = [(wl, b, pos[b], np.stack([qd[s][b] for s in range(steps)]), None) for b in range(B)]
+    pending = op.Pending(op.decode_job, jobs)
+    c = drive.make_cache(wl)
+    drive.fill(c, wl, n0)
+    outs, lses = [], []
+    for s in range(steps):
+        k, v = drive.kv_block(wl, list(pos[:, s]), 1, "cuda")
+        q = q_cpu[s].to("cuda")
+        lse = torch.empty((B, wl.n_q_heads), dtype=torch.float32, device="cuda")
+        if s % fused_every == 0:
+            out = c.decode_step(k[:, 0].contiguous(), v[:, 0].contiguous(), q, lse=lse)
+        else:
+            c.append(k, v)
+            out = c.decode(q, lse=lse)
+        outs.append(out.double().cpu().numpy())
+        lses.append(lse.cpu().numpy())
+    torch.cuda.synchronize()
+    ref = pending.get()
+    worst = (0.0, 0.0, -1)
+    for s in range(steps):
+        r = np.stack([ref[b][0][s] for b in range(B)])
+        rl = np.stack([ref[b][1][s] for b in range(B)])
+        err, rel = check_call(outs[s], r, lses[s], rl, f"{wl.name} step {s}")
+        if err > worst[0]:
+            worst = (err, rel, s)
+    print(f"{wl.name}: {steps} steps x {B} sequences x {wl.n_q_heads} heads, whole tensor; "
+          f"worst step {worst[2]}: max-abs {worst[0]:.3e} rel-l2 {worst[1]:.3e}")
+    return c, [n + steps for n in n0]
+
+
+def test_decode_p100_w4096_whole_tensor():
+    wl = configs.decode_p100_w4096()
+    c, n = decode_steps(wl, 2, fused_every=2)
+    check_exports(c, wl, n, wl.name)
+
+
+def test_decode_p512_w16384_whole_tensor():
+    wl = configs.decode_p512_w16384()
+    c, n = decode_steps(wl, 2, fused_every=2)
+    check_exports(c, wl, n, wl.name)
+
+
+def test_ragged_decode_64_steps_whole_tensor():
+    wl = configs.ragged_decode()
+    c, n = decode_steps(wl, wl.steps, fused_every=2)
+    check_exports(c, wl, n, wl.name)
+
+
+def test_decode_ragged_window_whole_tensor():
+    wl = configs.decode_ragged_window()
+    c, n = decode_steps(wl, 1)
+    check_exports(c, wl, n, wl.name)
+
+
+def test_decode_shared_p2000_whole_tensor():
+    # 64 runs of one 2000-token prompt read from one pool entry (sequence 0's values)
+    wl = configs.decode_shared_p2000()
+    B, P = wl.batch, wl.prefix[0]
+    n0 = [t - 1 for t in wl.start]
+    q_cpu = drive.queries(wl, n0, "cpu")
+    qd = q_cpu.double().numpy()
+    pending = op.Pending(op.decode_job, [(wl, b, np.array([n0[b]]), qd[b:b + 1], 0)
+                                         for b in range(B)])
+    c = drive.make_cache(wl, n_shared=1, shared_max=P, prefix_max=0)
+    drive.fill_one_prompt(c, wl, n0, shared=True)
+    k, v = drive.kv_block(wl, n0, 1, "cuda")
+    lse = torch.empty((B, wl.n_q_heads), dtype=torch.float32, device="cuda")
+    out = c.decode_step(k[:, 0].contiguous(), v[:, 0].contiguous(), q_cpu.to("cuda"), lse=lse)
+    o, lc = out.double().cpu().numpy(), lse.cpu().numpy()
+    ref = pending.get()
+    err, rel = check_call(o, np.concatenate([r[0] for r in ref]), lc,
+                          np.concatenate([r[1] for r in ref]), wl.name)
+    print(f"{wl.name}: {B} sequences whole tensor, max-abs {err:.3e} rel-l2 {rel:.3e}")
+
+
+def test_prefill_chunk512_whole_tensor():
+    wl = configs.prefill_chunk512()
+    B, C = wl.batch, wl.chunk
+    n0 = [t - 1 for t in wl.start]
+    q_cpu = drive.query_block(wl, n0, C, "cpu")
+    qd = q_cpu.double().numpy()
+    # jobs of 64 rows: 8 per sequence
+    R = 64
+    jobs = [(wl, b, np.arange(n0[b] + r, n0[b] + r + R), qd[b, r:r + R], None)
+            for b in range(B) for r in range(0, C, R)]
+    pending = op.Pending(op.decode_job, jobs)
+    c = drive.make_cache(wl, max_chunk=C)
+    drive.fill(c, wl, n0)
+    k, v = drive.kv_block(wl, n0, C, "cuda")
+    lse = torch.empty((B, C, wl.n_q_heads), dtype=torch.float32, device="cuda")
+    out = c.prefill(q_cpu.to("cuda"), k, v, lse=lse)
+    o, lc = out.double().cpu().numpy(), lse.cpu().numpy()
+    assert [c.seq_length(b) for b in range(B)] == [n + C for n in n0]
+    ref = pending.get()
+    per = C // R
+    r_out = np.stack([np.concatenate([ref[b * per + i][0] for i in range(per)]) for b in range(B)])
+    r_lse = np.stack([np.concatenate([ref[b * per + i][1] for i in range(per)]) for b in range(B)])
+    err, rel = check_call(o, r_out, lc, r_lse, wl.name)
+    print(f"{wl.name}: {B} x {C} rows x {wl.n_q_heads} heads whole tensor, max-abs {err:.3e} "
+          f"rel-l2 {rel:.3e}")
+    check_exports(c, wl, [n + C for n in n0], wl.name)

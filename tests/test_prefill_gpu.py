@@ -128,13 +128,3 @@ def test_float32_storage_rejected():
         c.prefill(q, k, k.clone())
     assert e.value.status == psa.PSA_ERR_ARG
     assert c.seq_length(0) == 0
-
-
-def test_prefill_chunk512_full_size():
-    wl = configs.prefill_chunk512()
-    n_hist = [t - 1 for t in wl.start]
-    c = drive.make_cache(wl, max_chunk=wl.chunk)
-    drive.fill(c, wl, n_hist)
-    rows = [0, 1, 2, 63, 64, 127, 200, 255, 256, 400, 510, 511]
-    err, rel = run_chunk(c, wl, n_hist, wl.chunk, rows=rows, seqs=[0, 3, 7], check_cache=True)
-    print(f"{wl.name}: max-abs {err:.2e} rel-l2 {rel:.2e}")

@@ -143,3 +143,40 @@ def test_pool_state_errors():
     assert e.value.status == psa.PSA_ERR_STATE
     c.reset(0, 2)                            # detaches
     c.prefix_load(0, kp[0].contiguous(), vp[0].contiguous())
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_long_shared_prefix_over_a_short_private_prefix(fused):
+    # prefix_max = 0 and a pool entry of 512 tokens with W = 128: an attached sequence sees
+    # 640 entries, five splits of 128, more than prefix_max + W alone would give room for.
+    # Each split's partial result needs its own workspace slot (a regression test of the
+    # workspace sizing), checked against the oracle at 128-entry splits and automatic ones.
+    P, W, B, Hkv, G = 512, 128, 3, 2, 4
+    wl = configs.Workload("shared-long", torch.bfloat16, B, Hkv * G, Hkv, 128, W, [P] * B,
+                          [1] * B, "decode")
+    c = drive.make_cache(wl, n_shared=1, shared_max=P, prefix_max=0)
+    kp, vp = drive.kv_rows_from(wl, [0], [0], P, "cuda")
+    c.prefix_load(0, kp[0].contiguous(), vp[0].contiguous())
+    for b in range(B):
+        c.attach(b, 0)
+    n_win = [300, 5, 128]
+    k, v = drive.kv_rows_from(wl, list(range(B)), [P] * B, max(n_win), "cuda")
+    c.append(k, v, n_new=n_win)
+    n = [P + x for x in n_win]
+    for tokens in (128, 0):
+        c.set_split_tokens(tokens)
+        k, v = drive.kv_rows_from(wl, list(range(B)), n, 1, "cuda")
+        q = drive.queries(wl, n, "cuda")
+        if fused:
+            out = c.decode_step(k[:, 0].contiguous(), v[:, 0].contiguous(), q)
+        else:
+            c.append(k, v)
+            out = c.decode(q)
+        torch.cuda.synchronize()
+        o = out.double().cpu().numpy()
+        qc = q.double().cpu().numpy()
+        for b in range(B):
+            hist = drive.composite_history(wl, 0, b, P)
+            ref, _ = attn.decode_query(qc[b], n[b], hist, P, W, Hkv, wl.rope_base, wl.scale)
+            tol_check(o[b], ref, f"split {tokens} seq {b}")
+        n = [x + 1 for x in n]
