@@ -129,3 +129,17 @@ def test_tiny_fp32_cache_every_step():
         k, v = drive.kv_block(wl, [n - 1], 1, "cuda")
         c.append(k, v)
         check_seq(c, wl, 0, n)
+
+
+@pytest.mark.parametrize("D,base", [(64, 10000.0), (128, 10000.0), (128, 500000.0)])
+def test_rotation_frequencies_are_the_nearest_doubles(D, base):
+    # The cache's theta table (the library's work region starts with it) against the
+    # oracle's correctly rounded base^(-2i/D), bit for bit: an angle p * theta_i of a late
+    # position moves by p ulps of theta when theta is one ulp off.
+    from oracle import rope
+    wl = configs.Workload("theta", torch.bfloat16, 1, 8, 8, D, 16, [0], [1], "decode",
+                          rope_base=base)
+    c = drive.make_cache(wl)
+    off = c.layout.work_offset
+    got = c.mem[off:off + D // 2 * 8].cpu().numpy().view(np.float64)
+    np.testing.assert_array_equal(got.view(np.uint64), rope.inv_freq(D, base).view(np.uint64))

@@ -47,6 +47,7 @@ def check_call(out: np.ndarray, ref: np.ndarray, lse=None, ref_lse=None, what=""
 def check_exports(c, wl, n_final, what):
     """Every sequence's exported cache against the list model, bit for bit."""
     want = op.run(op.expected_view_job, [(wl, b, n_final[b], "bf16") for b in range(wl.batch)])
+    print(f"{what}: list model's views ready", flush=True)
     bad = []
     for b in range(wl.batch):
         k_e, v_e, pos_e = c.export(b)
@@ -61,9 +62,13 @@ def check_exports(c, wl, n_final, what):
                                                 drive.hist_provider(wl, b), wl.rope_base, "bf16")
         detail = f"count {len(pos_e)} vs {len(pos)}"
         if len(pos) == len(pos_e):
+            kb = bits(k_e)
+            d = np.argwhere(kb != kbits)
             detail += (f", positions differ at {int((pos_e.numpy() != pos).sum())}, key bits at "
-                       f"{int((bits(k_e) != kbits).sum())}, values at "
-                       f"{int((v_e.double().numpy() != vref).sum())} elements")
+                       f"{len(d)}, values at {int((v_e.double().numpy() != vref).sum())} elements")
+            for r, h, e in d[:4]:
+                detail += (f"; entry {r} position {pos[r]} head {h} dim {e}: {kb[r, h, e]:#06x} "
+                           f"vs {kbits[r, h, e]:#06x} ({int(kb[r, h, e]) - int(kbits[r, h, e])} bf16 ulp)")
         pytest.fail(f"{what}: {len(bad)} sequences differ from the list model (first {b}: {detail})")
     print(f"{what}: {wl.batch} exported caches bit-exact")
 
@@ -80,6 +85,7 @@ def decode_steps(wl, steps: int, fused_every: int = 1):
     pending = op.Pending(op.decode_job, jobs)
     c = drive.make_cache(wl)
     drive.fill(c, wl, n0)
+    print(f"{wl.name}: filled {sum(n0)} tokens", flush=True)
     outs, lses = [], []
     for s in range(steps):
         k, v = drive.kv_block(wl, list(pos[:, s]), 1, "cuda")
@@ -93,6 +99,7 @@ def decode_steps(wl, steps: int, fused_every: int = 1):
         outs.append(out.double().cpu().numpy())
         lses.append(lse.cpu().numpy())
     torch.cuda.synchronize()
+    print(f"{wl.name}: {steps} GPU steps done; waiting for the oracle", flush=True)
     ref = pending.get()
     worst = (0.0, 0.0, -1)
     for s in range(steps):

@@ -1,5 +1,9 @@
 """Pins of oracle.rope: the complex-number form of the rotation, norm preservation,
-identity at position 0, and logits that depend only on the relative offset."""
+identity at position 0, logits that depend only on the relative offset, and theta_i as the
+float64 nearest to base^(-2i/D)."""
+import math
+
+import mpmath
 import numpy as np
 
 from oracle import rope
@@ -9,8 +13,7 @@ def complex_rotate(x, pos, base):
     """Rotation written as complex multiplication: z_i = x_i + 1j * x_{i+D/2}, times e^{1j p theta_i}."""
     D = x.shape[-1]
     h = D // 2
-    i = np.arange(h)
-    theta = float(base) ** (-2.0 * i / D)
+    theta = np.array([math.pow(float(base), (-2.0 * i) / D) for i in range(h)])
     z = x[..., :h] + 1j * x[..., h:]
     z = z * np.exp(1j * (np.asarray(pos, dtype=np.float64)[..., None] * theta))
     return np.concatenate([z.real, z.imag], axis=-1)
@@ -65,3 +68,28 @@ def test_inv_freq_closed_form():
     assert th[0] == 1.0
     np.testing.assert_allclose(th[1:] / th[:-1], 10000.0 ** (-2.0 / 128), rtol=1e-14)
     np.testing.assert_allclose(th[-1], 10000.0 ** (-126.0 / 128), rtol=1e-15)
+
+
+def test_inv_freq_is_the_nearest_double():
+    # correct rounding by its definition: the real value lies within half an ulp of theta_i
+    # (checked at 600 bits, twice the oracle's working precision)
+    for D in (64, 128):
+        for base in (10000.0, 500000.0):
+            th = rope.inv_freq(D, base)
+            with mpmath.workprec(600):
+                for i, t in enumerate(th):
+                    exact = mpmath.power(mpmath.mpf(base), mpmath.mpf(-2 * i) / D)
+                    half = (mpmath.mpf(math.nextafter(t, math.inf)) - mpmath.mpf(t)) / 2
+                    assert abs(exact - mpmath.mpf(t)) <= half, (D, base, i)
+
+
+def test_inv_freq_special_values():
+    th = rope.inv_freq(128, 10000.0)
+    assert th[32] == 0.01                      # 10000^(-1/2)
+    # a faithful power routine can round this one the other way (one ulp below)
+    assert th[2] == float.fromhex("0x1.7ff2224115d9ap-1")
+    # the platform's correctly rounded pow agrees at every frequency of the tested bases
+    for D in (64, 128):
+        for base in (10000.0, 500000.0, 1e6):
+            th = rope.inv_freq(D, base)
+            assert all(math.pow(base, (-2.0 * i) / D) == th[i] for i in range(D // 2))
