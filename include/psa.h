@@ -148,22 +148,26 @@ typedef struct {
 } psa_layout;
 
 /* Device bytes the caller must provide for a cache described by *desc (0 if *desc is
- * invalid; psa_last_error() then says why). Host only; enqueues nothing. */
+ * invalid; psa_last_error() then says why). Host only; enqueues nothing. Memory management
+ * of the library: no passage of the pages defines it. */
 size_t psa_cache_bytes(const psa_cache_desc *desc);
 
 /* Fill *out with the layout of a cache described by *desc. Host only.
- * Returns PSA_ERR_ARG for a null pointer or an invalid description. */
+ * Returns PSA_ERR_ARG for a null pointer or an invalid description. (Library
+ * infrastructure: defined by no passage of the pages.) */
 int psa_cache_layout(const psa_cache_desc *desc, psa_layout *out);
 
 /* Create a cache over caller-owned device memory dev_mem (>= psa_cache_bytes(desc)
- * bytes, 256-byte aligned) on the current HIP device. Initialises every slot tag to
+ * bytes, 256-byte aligned) on the current HIP device (library infrastructure: defined by
+ * no passage of the pages; the empty cache is [KV-Lean] 2.3's empty window list). Initialises every slot tag to
  * -1 and every sequence to "not started", then waits for `stream`.
  * On success *out receives a new handle; on error *out is left unchanged.
  * The memory stays owned by the caller and must outlive the handle. */
 int psa_cache_create(const psa_cache_desc *desc, void *dev_mem, size_t bytes, psa_stream stream,
                      psa_cache **out);
 
-/* Release the host handle (the device memory is the caller's). NULL is accepted. */
+/* Release the host handle (the device memory is the caller's). NULL is accepted.
+ * (Library infrastructure: defined by no passage of the pages.) */
 int psa_cache_destroy(psa_cache *cache);
 
 /* Start (or restart) sequence `seq` with a pinned prefix of prefix_len tokens
@@ -264,9 +268,12 @@ int psa_decode_step(psa_cache *cache, const void *k, const void *v, const void *
                     float *lse, psa_stream stream);
 
 /* Chunked prefill: every sequence takes `chunk` new tokens at positions
- * len_b .. len_b + chunk - 1; query row c (at p = len_b + c) attends to the prefix,
- * the window of p and the chunk's own tokens up to p (a chunk equals `chunk`
- * consecutive decode steps). Then the chunk is appended as by psa_append.
+ * len_b .. len_b + chunk - 1; query row c (at p = len_b + c) attends to A(p + 1) of
+ * [PS] 03: the prefix, the window of p and the chunk's own tokens up to p. The pages never
+ * discuss chunks; the reading taken is that a chunk equals `chunk` consecutive decode
+ * steps. Key tiles no row of a query block sees are never loaded, tiles every row sees
+ * entirely run unmasked, and only partially covered tiles are masked per element ([PS] 06,
+ * the block-level then token-level filter). Then the chunk is appended as by psa_append. 
  * q, out: [B][chunk][H_q][D]; k, v: [B][chunk][H_kv][D]; lse: [B][chunk][H_q] float32
  * or NULL. 1 <= chunk <= max_chunk. Errors: PSA_ERR_STATE if a sequence was never
  * reset or (paged) the pool has fewer free blocks than the chunk needs;
@@ -328,16 +335,21 @@ int psa_train_bwd(const psa_train_desc *desc, const int32_t *prefix_host,
                   void *dv, void *workspace, size_t workspace_bytes, psa_stream stream);
 
 /* History length of `seq` from the host mirror (-1 if seq is out of range or the
- * sequence was never reset). Host only. */
+ * sequence was never reset). Host only. (Library infrastructure: defined by no passage of
+ * the pages.) */
 int64_t psa_seq_length(const psa_cache *cache, int32_t seq);
 
 /* Visible entries per decode split (the work unit of one workgroup); 0 restores the
- * automatic choice. Must be 0 or >= 128. Results are the same up to float32 rounding
+ * automatic choice. (A tuning knob of this library's split-KV decode: defined by no passage
+ * of the pages.) Must be 0 or >= 128. Results are the same up to float32 rounding
  * order for any value. Host only. */
 int psa_set_split_tokens(psa_cache *cache, int32_t tokens);
 
 /* Kernel timing with HIP events recorded on the launch stream around each kernel.
- * enable != 0 starts recording (and clears earlier totals), 0 stops it. */
+ * enable != 0 starts recording (and clears earlier totals), 0 stops it. Each figure brackets
+ * one launch, so it includes the launch's ramp-up and drain and the sum over a step's
+ * kernels can exceed the step's own time. (Measurement infrastructure: defined by no
+ * passage of the pages.) */
 int psa_profile(psa_cache *cache, int32_t enable);
 
 /* Kernel ids for psa_profile_read. */
@@ -354,10 +366,12 @@ enum {
  * the number of launches of kernel `kernel` since profiling was enabled. */
 int psa_profile_read(psa_cache *cache, int32_t kernel, double *total_ms, int64_t *launches);
 
-/* Static text of a status code. */
+/* Static text of a status code. (Library infrastructure: defined by no passage of the
+ * pages.) */
 const char *psa_status_string(int status);
 
-/* Text of the last error on this thread (empty if none). */
+/* Text of the last error on this thread (empty if none). (Library infrastructure: defined
+ * by no passage of the pages.) */
 const char *psa_last_error(void);
 
 #ifdef __cplusplus
