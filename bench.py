@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--prefill-calls", type=int, default=30)
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--train-calls", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other decode workloads and the flat-in-t sweep")
+    ap.add_argument("--only", default="", choices=["", "prefill", "train"],
+                    help="run only the chunked-prefill or the training benchmark and print its "
+                         "JSON (for profiler runs of one kernel family)")
     ap.add_argument("--step", default="fused", choices=["fused", "separate"],
                     help="decode step as one psa_decode_step call (append + decode in one "
                          "launch) or as psa_append then psa_decode_attn")
@@ -283,6 +288,148 @@ def bench_train(calls: int, warmup: int = 2):
                          "kernel": "backward (rowdot + dkdv + dq)", "flops_per_launch": 5 * unit}}
 
 
+def fill_timing(cache, wl, n_hist, block=4096) -> None:
+    """Bring every sequence to n_hist[b] tokens through real appends (eviction included),
+    with one seeded [B][block][H_kv][D] block of values appended over and over: the
+    timing-only sweeps read the same visible set whatever the values, and drawing every
+    position of a 131072-token history would dominate the run."""
+    import torch
+
+    from synth import drive
+
+    B = wl.batch
+    for b in range(B):
+        cache.reset(b, wl.prefix[b])
+        if wl.windows is not None:
+            cache.set_window(b, wl.windows[b])
+    k, v = drive.kv_block(wl, [0] * B, block, "cuda")
+    done = [0] * B
+    while any(d < n for d, n in zip(done, n_hist)):
+        counts = [min(block, n - d) for d, n in zip(done, n_hist)]
+        cache.append(k, v, n_new=counts)
+        done = [d + c for d, c in zip(done, counts)]
+    torch.cuda.synchronize()
+
+
+def time_steps(c, wl, n0, warmup: int, steps: int, fused: bool = True):
+    """warmup + steps decode steps from histories n0 (the state advances one token per
+    step), the timed steps between two events; then `steps` more with per-kernel events.
+    Returns (ms per step, {kernel: (total ms, launches)}, visible entries of the first and
+    last profiled step)."""
+    import torch
+
+    import prefix_pinned_sliding_amd as psa
+    from synth import drive
+
+    total = warmup + 2 * steps
+    ks, vs, qs = [], [], []
+    for i in range(total):
+        k, v = drive.kv_block(wl, [n + i for n in n0], 1, "cuda")
+        ks.append(k[:, 0].contiguous() if fused else k)
+        vs.append(v[:, 0].contiguous() if fused else v)
+        qs.append(drive.queries(wl, [n + i for n in n0], "cuda"))
+    out = torch.empty_like(qs[0])
+
+    def step(i):
+        if fused:
+            c.decode_step(ks[i], vs[i], qs[i], out)
+        else:
+            c.append(ks[i], vs[i])
+            c.decode(qs[i], out)
+
+    c.decode(qs[0], out)     # untimed: loads the kernels, only reads the cache
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(warmup, warmup + steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    c.profile(True)
+    for i in range(warmup + steps, total):
+        step(i)
+    torch.cuda.synchronize()
+    times = {name: c.profile_read(k) for k, name in psa.KERNEL_NAMES.items()}
+    c.profile(False)
+    vis = (visible_entries(wl, [n + warmup + steps + 1 for n in n0]),
+           visible_entries(wl, [n + total for n in n0]))
+    return ms, times, vis
+
+
+def decode_roofline(wl, times, vis):
+    elem = 2 if str(wl.dtype) == "torch.bfloat16" else 4
+    dec_ms, dec_n = times["decode_partial"]
+    dec_s = dec_ms / dec_n / 1e3
+    launch_bytes = 0.5 * (vis[0] + vis[1]) * wl.n_kv_heads * wl.head_dim * 2 * elem
+    achieved = launch_bytes / dec_s / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "kernel": "decode_partial",
+            "kernel_avg_us": dec_s * 1e6, "bytes_per_launch": launch_bytes}
+
+
+def bench_decode_config(name: str, warmup: int, steps: int):
+    """Another decode workload's fused step: µs per step, tokens/s and the decode kernel's
+    roofline. Histories are filled with real seeded values (drive.fill)."""
+    import torch
+
+    from synth import configs, drive
+
+    wl = configs.by_name(name)
+    n0 = [t - 1 for t in wl.start]
+    c = drive.make_cache(wl)
+    drive.fill(c, wl, n0)
+    ms, times, vis = time_steps(c, wl, n0, warmup, steps)
+    del c
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "warmup": warmup, "steps": steps, "ms_per_step": ms,
+            "tokens_per_s": wl.batch / (ms / 1e3),
+            "visible_tokens_per_step": 0.5 * (vis[0] + vis[1]),
+            "roofline": decode_roofline(wl, times, vis),
+            "kernels_avg_us": {k: (t / n * 1e3 if n else None) for k, (t, n) in times.items()}}
+
+
+FLAT_T = (2148, 4196, 8392, 32768, 131072)
+
+
+def bench_flat_in_t(warmup: int = 10, steps: int = 50):
+    """The default decode shape (64 sequences, P = 100, W = 4096) at several t: the step
+    must cost the same once the window is full ([PS] 04: per-step cost O((P + W) d),
+    independent of t). One cache is brought from one t to the next by appends."""
+    import torch
+
+    from synth import configs, drive
+
+    wl = configs.decode_p100_w4096()
+    B = wl.batch
+    c = drive.make_cache(wl)
+    res, n = {}, 0
+    for t in FLAT_T:
+        target = t - 1
+        if n == 0:
+            fill_timing(c, wl, [target] * B)
+        elif target > n:
+            k, v = drive.kv_block(wl, [0] * B, 4096, "cuda")
+            while n < target:
+                r = min(4096, target - n)
+                c.append(k, v, n_new=[r] * B)
+                n += r
+        n = target
+        ms, times, vis = time_steps(c, wl, [n] * B, warmup, steps)
+        n += warmup + 2 * steps
+        res[str(t)] = {"us_per_step": ms * 1e3,
+                       "decode_partial_us": times["decode_partial"][0] / times["decode_partial"][1] * 1e3,
+                       "visible_per_sequence": vis[1] // B}
+    del c
+    torch.cuda.empty_cache()
+    full = [res[str(t)]["us_per_step"] for t in FLAT_T if t >= 4196]
+    return {"workload": "decode-bf16-B64-P100-W4096 at several t", "warmup": warmup,
+            "steps": steps, "t": res,
+            "spread_full_window": (max(full) - min(full)) / (sum(full) / len(full))}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -294,6 +441,13 @@ def main():
     import torch
 
     from synth import configs, drive, gen
+
+    if args.only:
+        torch.cuda.set_device(0)
+        res = bench_prefill(args.prefill_calls) if args.only == "prefill" else \
+            bench_train(args.train_calls)
+        print(json.dumps({args.only: res}), flush=True)
+        return
 
     if args.workload == "decode_p100_w4096":
         wl = configs.decode_p100_w4096(t=args.t) if args.t else configs.decode_p100_w4096()
@@ -457,6 +611,15 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] training attention", file=sys.stderr, flush=True)
         result["train"] = bench_train(args.train_calls)
+
+    if not args.no_extra and args.workload == "decode_p100_w4096" and not args.t:
+        torch.cuda.empty_cache()
+        print("[bench] decode P=512 W=16384", file=sys.stderr, flush=True)
+        result["decode_p512_w16384"] = bench_decode_config("decode_p512_w16384", 10, 50)
+        print("[bench] ragged decode B=256", file=sys.stderr, flush=True)
+        result["ragged_decode"] = bench_decode_config("ragged_decode", 0, 64)
+        print("[bench] flat in t", file=sys.stderr, flush=True)
+        result["flat_in_t"] = bench_flat_in_t()
 
     if cpu is not None:
         result["cpu_baseline"] = cpu
