@@ -334,6 +334,23 @@ int psa_train_bwd(const psa_train_desc *desc, const int32_t *prefix_host,
                   const void *out, const float *lse, const void *dout, void *dq, void *dk,
                   void *dv, void *workspace, size_t workspace_bytes, psa_stream stream);
 
+/* psa_train_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * kernels and results as psa_train_bwd, without the workspace argument. Its scratch (the
+ * sequences' prefix and length table and the float32 row dots sum_d dout * out,
+ * [B][T][H_q]) lives in a static device array of PSA_TRAIN_STATIC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends; the call itself
+ * allocates and frees nothing. Every call on one GPU shares that GPU's array and leaves
+ * its contents behind (nothing in it needs to start at zero: each call writes every entry
+ * it reads), so calls that overlap in time on one GPU (other streams, other threads) race.
+ * Errors: as psa_train_bwd; PSA_ERR_ARG when psa_train_workspace_bytes(desc) exceeds the
+ * array (B * T * H_q above about 4.19 million rows), before anything is enqueued. */
+#define PSA_TRAIN_STATIC_SCRATCH_BYTES (16u << 20)
+int psa_train_bwd_noalloc(const psa_train_desc *desc, const int32_t *prefix_host,
+                          const int32_t *len_host, const void *q, const void *k, const void *v,
+                          const void *out, const float *lse, const void *dout, void *dq,
+                          void *dk, void *dv, psa_stream stream);
+
 /* History length of `seq` from the host mirror (-1 if seq is out of range or the
  * sequence was never reset). Host only. (Library infrastructure: defined by no passage of
  * the pages.) */

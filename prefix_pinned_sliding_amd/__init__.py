@@ -114,6 +114,8 @@ def _load() -> ctypes.CDLL:
         "psa_train_fwd": (ctypes.c_int, [ctypes.POINTER(TrainDesc), P, P, P, P, P, P, P, P, SZ, P]),
         "psa_train_bwd": (ctypes.c_int, [ctypes.POINTER(TrainDesc), P, P, P, P, P, P, P, P, P, P,
                                          P, P, SZ, P]),
+        "psa_train_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(TrainDesc), P, P, P, P, P, P, P,
+                                                 P, P, P, P, P]),
         "psa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "psa_last_error": (ctypes.c_char_p, []),
     }
@@ -429,4 +431,24 @@ class TrainAttention:
         _check(lib.psa_train_bwd(ctypes.byref(self.desc), pre, ln, _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(self.ws), self.ws.numel(), _stream(stream)), "psa_train_bwd")
+        return dq, dk, dv
+
+    def backward_noalloc(self, q, k, v, out, lse, dout, prefix, lens=None, dq=None, dk=None,
+                         dv=None, stream=None):
+        """backward() through psa_train_bwd_noalloc: the library's static scratch instead of
+        this object's workspace (the outputs must be given to allocate nothing here)."""
+        for name, t, hh in (("q", q, self.Hq), ("k", k, self.Hkv), ("v", v, self.Hkv),
+                            ("out", out, self.Hq), ("dout", dout, self.Hq)):
+            self._check(t, name, hh)
+        self._check(lse, "lse", self.Hq, torch.float32)
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        for name, t, hh in (("dq", dq, self.Hq), ("dk", dk, self.Hkv), ("dv", dv, self.Hkv)):
+            self._check(t, name, hh)
+        pre, ln = self._seq(prefix, lens)
+        _check(lib.psa_train_bwd_noalloc(ctypes.byref(self.desc), pre, ln, _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), _stream(stream)),
+               "psa_train_bwd_noalloc")
         return dq, dk, dv

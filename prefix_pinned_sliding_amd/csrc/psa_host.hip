@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1092,6 +1093,64 @@ PSA_API int psa_train_bwd(const psa_train_desc* desc, const int32_t* prefix_host
         return fail(PSA_ERR_ARG, "an input or output pointer is NULL");
     return train_run(desc, prefix_host, len_host, q, k, v, out, nullptr, const_cast<float*>(lse),
                      dout, dq, dk, dv, workspace, workspace_bytes, stream, true);
+}
+
+// ---- psa_train_bwd_noalloc: the backward pass with its scratch in a static device array --
+// For callers that cannot allocate device memory. The array's name is a host-side stand-in
+// in host code: its device address is taken once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever passed to kernels.
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)PSA_TRAIN_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of `scratch` (resolved on first use).
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(PSA_ERR_ARG, "device index beyond the static scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr || ((uintptr_t)p & 255u) != 0)
+            return fail(PSA_ERR_HIP, "static scratch has no 256-byte aligned device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PSA_OK;
+}
+
+}  // namespace
+
+PSA_API int psa_train_bwd_noalloc(const psa_train_desc* desc, const int32_t* prefix_host,
+                                  const int32_t* len_host, const void* q, const void* k,
+                                  const void* v, const void* out, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv,
+                                  psa_stream stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr ||
+        dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+        return fail(PSA_ERR_ARG, "an input or output pointer is NULL");
+    TrainWs ws;
+    const char* why = nullptr;
+    if (!train_check(desc, &ws, &why)) return fail(PSA_ERR_ARG, why);
+    if (ws.total > kStaticScratchBytes)
+        return fail(PSA_ERR_ARG, "the backward pass needs " + std::to_string(ws.total) +
+                                     " bytes of scratch; the static scratch holds " +
+                                     std::to_string(kStaticScratchBytes));
+    void* w = nullptr;
+    const int rc = scratch_of_current_device(&w);
+    if (rc != PSA_OK) return rc;
+    return train_run(desc, prefix_host, len_host, q, k, v, out, nullptr, const_cast<float*>(lse),
+                     dout, dq, dk, dv, w, kStaticScratchBytes, stream, true);
 }
 
 PSA_API const char* psa_status_string(int status) {

@@ -246,3 +246,17 @@ def test_counter_file_is_tied_to_kernel_code_not_comments(tmp_path):
     c.write_text(src.replace("kRescaleSlack = 8.0f", "kRescaleSlack = 7.0f"))
     assert bench.source_hash(str(a)) == bench.source_hash(str(b))
     assert bench.source_hash(str(a)) != bench.source_hash(str(c))
+
+
+def test_noalloc_backward_rejects_shapes_beyond_its_static_scratch(psa):
+    # B * T * H_q float32 row dots above PSA_TRAIN_STATIC_SCRATCH_BYTES: refused on the host,
+    # before any device call (the pointers are never touched)
+    d = psa.TrainDesc(1, 1 << 20, 8, 8, 128, 4096, 0.0, 0)
+    assert psa.lib.psa_train_workspace_bytes(ctypes.byref(d)) > 16 << 20
+    pre = (ctypes.c_int32 * 1)(0)
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(9)]
+    rc = psa.lib.psa_train_bwd_noalloc(ctypes.byref(d), pre, None, *fake, None)
+    assert rc == psa.PSA_ERR_ARG
+    assert "static scratch" in psa.lib.psa_last_error().decode()
+    d.n_q_heads = 12          # and the ordinary shape checks still come first
+    assert psa.lib.psa_train_bwd_noalloc(ctypes.byref(d), pre, None, *fake, None) == psa.PSA_ERR_ARG
