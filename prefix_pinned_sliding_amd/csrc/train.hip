@@ -229,12 +229,23 @@ __global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
     a.di[idx] = acc;
 }
 
-// Unpadded LDS tiles with the 16-byte chunk c of row r stored at chunk c ^ chunk_swz(r).
-// For rows r .. r + 7, chunk_swz is a permutation of 0 .. 7, so 16-byte row reads (8 lanes
-// on 8 consecutive rows, same logical chunk) fall in 8 different 16-byte bank groups; for
-// 4 consecutive rows chunk_swz / 2 is a permutation of 0 .. 3, so the 4 chunk pairs a
-// transposing read takes from 4 rows do too.
-__device__ __forceinline__ int chunk_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// Unpadded LDS tiles with the 16-byte chunk c of row r stored at chunk c ^ chunk_swz<D>(r),
+// a function of r mod 16. The reads: 16-byte row reads (16 lanes on 16 consecutive rows, one
+// logical chunk each) and transposing 8-byte reads (each 16-lane group takes a chunk pair
+// from 4 consecutive rows). The swizzle puts every such read on distinct banks whether the
+// LDS serves 16-byte reads 8 lanes at a time from 32 four-byte banks (and 8-byte reads 16 at
+// a time), or 16 lanes at a time from 64 banks (8-byte reads 32 at a time): for D = 128
+// (256-byte rows) it is a permutation of 0 .. 15 on rows 0 .. 15, a permutation of 0 .. 7
+// modulo 8 on rows 0 .. 7 and on 8 .. 15, and its half is distinct modulo 8 on each 8-row
+// half and modulo 4 on each 4-row quarter; for D = 64 (128-byte rows, two per 256 bytes) the
+// same holds on the even and the odd rows separately. (An 8-row swizzle leaves rows r and
+// r + 8 on the same banks when 64 banks serve 16 lanes.)
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+    const int b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+    if constexpr (D == 128) return 2 * (r & 3) + (b2 ^ b3) + 8 * b2;
+    else return ((5 * (r & 7)) ^ b3) & 7;
+}
 
 // One wave-wide direct load into LDS: lane l's 16 bytes at `g` land at LDS byte address
 // lds + 16 l (global_load_lds_dwordx4, LDS base in M0). The compiler does not see this
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         for (int x = 0; x < NPW; ++x) {
             const int blk = wave * NPW + x;
             const int r = blk * RPL + lane / CPR;
-            const size_t e = row_off(i0, min(r, last)) + ((lane % CPR) ^ chunk_swz(r)) * 8;
+            const size_t e = row_off(i0, min(r, last)) + ((lane % CPR) ^ chunk_swz<D>(r)) * 8;
             const uint32_t o = (uint32_t)(buf * kBR * D * 2 + blk * 1024);
             lds_dma16(q_lds + o, a.q + e);
             lds_dma16(g_lds + o, a.dout + e);
@@ -338,9 +349,9 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
             di_r = a.di[ri];
         }
     };
-    // this lane's chunk swizzles: row reads (rows = l16 mod 8) and transposing reads
-    // (rows = 4 lg + l16 / 4 mod 8)
-    const int swz_row = chunk_swz(l16), swz_tr = chunk_swz(4 * lg + l16 / 4);
+    // this lane's chunk swizzles: row reads (rows = l16 mod 16) and transposing reads
+    // (rows = 4 lg + l16 / 4 mod 16)
+    const int swz_row = chunk_swz<D>(l16), swz_tr = chunk_swz<D>(4 * lg + l16 / 4);
     if (k0 < i_end) issue(k0, 0);
     int buf = 0;
 #pragma unroll 1
@@ -506,15 +517,15 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
             const int blk = wave * NPW + x;
             const int r = blk * RPL + lane / CPR;
             const size_t e = (kv0 + (size_t)(s0 + min(r, last)) * a.Hkv) * D +
-                             ((lane % CPR) ^ chunk_swz(r)) * 8;
+                             ((lane % CPR) ^ chunk_swz<D>(r)) * 8;
             const uint32_t o = (uint32_t)(buf * kBN * D * 2 + blk * 1024);
             lds_dma16(k_lds + o, a.k + e);
             lds_dma16(v_lds + o, a.v + e);
         }
     };
-    // this lane's chunk swizzles: row reads (rows = l16 mod 8) and transposing reads
-    // (rows = 4 lg + l16 / 4 mod 8)
-    const int swz_row = chunk_swz(l16), swz_tr = chunk_swz(4 * lg + l16 / 4);
+    // this lane's chunk swizzles: row reads (rows = l16 mod 16) and transposing reads
+    // (rows = 4 lg + l16 / 4 mod 16)
+    const int swz_row = chunk_swz<D>(l16), swz_tr = chunk_swz<D>(4 * lg + l16 / 4);
     int seg = 0, t0 = -kBN, buf = 0;
     bool have = wk.next(seg, t0);
     if (have) issue(seg, t0, 0);
