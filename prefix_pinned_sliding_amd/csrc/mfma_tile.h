@@ -197,6 +197,69 @@ __device__ __forceinline__ bool tile_max(f32x4 (&s)[2][kTileKeys / 16],
     return moved;
 }
 
+// tile_max for a reference pinned at 0 (prefill, products already in the log2 domain).
+// The values subtracted from the logits, mb, stay 0 for every row whose logits stay within
+// +-kRefRange of 0: then exp2 of a product is at most 2^kRefRange, the row sums and outputs
+// stay far inside float32, and no tile needs a rescale. m holds the trigger, mb + kRefRange
+// once the row has seen a key (kNeg before). A row's first visible tile keeps mb = 0 if its
+// maximum lies in [-kRefRange, kRefRange], else takes that maximum; a later tile moves mb
+// (rescaling O and l) only past mb + kRefRange. Returns whether some row of the wave changed
+// its reference (then exponentials taken against the old one are stale).
+constexpr float kRefRange = 64.0f;
+
+template <int D>
+__device__ __forceinline__ bool tile_max_pinned(f32x4 (&s)[2][kTileKeys / 16],
+                                                SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
+                                                int ct0, int t1, int P, int W, int lg, bool masked) {
+    constexpr int DB = D / 16, KB = kTileKeys / 16;
+    float ml[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        if (masked) {
+            const int p = row_pos[rb];
+            int jb = ct0 + 4 * lg;
+            asm volatile("" : "+v"(jb));   // keeps the mask's arithmetic inside this branch
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = jb + kb * 16 + i;
+                    const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
+                    s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
+                }
+        }
+        ml[rb] = fmaxf(s[rb][0][0], s[rb][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = (kb == 0 ? 2 : 0); i < 4; i += 2)
+                ml[rb] = __builtin_fmaxf(__builtin_fmaxf(ml[rb], s[rb][kb][i]), s[rb][kb][i + 1]);
+    }
+    if (!__any(ml[0] + st.mb[0] > st.m[0] || ml[1] + st.mb[1] > st.m[1])) return false;
+    bool changed = false;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float mt = row_max4(ml[rb]) + st.mb[rb];   // absolute tile max of the row
+        if (mt > st.m[rb]) {
+            const bool first = st.m[rb] == kNeg;
+            const float nb = first && mt <= kRefRange && mt >= -kRefRange ? 0.f : mt;
+            if (nb != st.mb[rb]) {
+                const float f = __builtin_amdgcn_exp2f(st.mb[rb] - nb);
+                const float shift = nb - st.mb[rb];
+                st.l[rb] *= f;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) st.o[rb][db] *= f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[rb][kb] -= shift;
+                st.mb[rb] = nb;
+                changed = true;
+            }
+            st.m[rb] = nb + kRefRange;
+        }
+    }
+    return __any(changed);
+}
+
 template <int D>
 __device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][kTileKeys / 32], f32x4 (&s)[2][kTileKeys / 16],
                                              SoftmaxRows<D / 16>& st, const int (&row_pos)[2],
@@ -256,7 +319,7 @@ __device__ __forceinline__ void tile_exp_half(bf16x8 (&pb)[2], const f32x4 (&s)[
 // operands of keys 0-31 (`pb0`, exponentials against the running max from before this
 // tile) taken between those products. pb0 holds for the tile unless the tile is masked or
 // moves the running max (tile_max); the caller recomputes it then.
-template <int D>
+template <int D, bool ZERO = false>
 __device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x8 (&pb0)[2],
                                             const SoftmaxRows<D / 16>& st,
                                             const bf16x8 (&qop)[2][D / 32], const uint16_t* k_s,
@@ -264,7 +327,9 @@ __device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x
     constexpr int KS = D / 32, KB = kTileKeys / 16;
     constexpr int KSTR = D + kKPad;
     static_assert(KB == 4 && 16 % KS == 0, "two halves of two 16-key blocks");
-    const float s0 = -st.mb[0] * inv_sc, s1 = -st.mb[1] * inv_sc;
+    // ZERO: every row of the wave has reference 0, so the accumulators start from the
+    // products' inline constant 0 instead of 32 register moves
+    const float s0 = ZERO ? 0.f : -st.mb[0] * inv_sc, s1 = ZERO ? 0.f : -st.mb[1] * inv_sc;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         s[0][kb] = f32x4{s0, s0, s0, s0};
@@ -360,6 +425,32 @@ __device__ __forceinline__ void tile_exp_pv(SoftmaxRows<D / 16>& st, const f32x4
 // 32-63's during keys 0-31's PV products (tile_exp_pv). It pays where the products arrive
 // in the log2 domain (sc = 1): about 1.5% on the prefill kernel; the training forward pass
 // ran 3% slower with it.
+// The prefill's tile: products in the log2 domain (sc = 1) and the softmax reference pinned
+// at 0 (tile_max_pinned). The accumulators always start from the products' inline constant
+// 0, so keys 0-31's exponentials taken during the products are against reference 0; a wave
+// with some row on another reference (`shifted`, wave-uniform) subtracts it afterwards and
+// takes those exponentials again.
+template <int D>
+__device__ __forceinline__ void tile_step_pinned(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
+                                                 const uint16_t* k_s, const uint16_t* v_s,
+                                                 const int (&row_pos)[2], int ct0, int t1, int P,
+                                                 int W, int l16, int lg, bool masked,
+                                                 bool mid_barrier, bool shifted) {
+    f32x4 s[2][kTileKeys / 16];
+    bf16x8 pb0[2];
+    tile_qk_exp<D, true>(s, pb0, st, qop, k_s, l16, lg, 1.f, 1.f);
+    if (mid_barrier) __syncthreads();
+    if (shifted) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < kTileKeys / 16; ++kb) s[rb][kb] -= st.mb[rb];
+    }
+    if (tile_max_pinned<D>(s, st, row_pos, ct0, t1, P, W, lg, masked) || masked || shifted)
+        tile_exp_half(pb0, s, 0, 1.f);
+    tile_exp_pv<D>(st, s, pb0, v_s, l16, lg, 1.f);
+}
+
 template <int D, bool kSplitExp = false>
 __device__ __forceinline__ void tile_step(SoftmaxRows<D / 16>& st, const bf16x8 (&qop)[2][D / 32],
                                           const uint16_t* k_s, const uint16_t* v_s,

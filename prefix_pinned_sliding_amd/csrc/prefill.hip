@@ -387,8 +387,8 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
             }
             const bool full = (ct0 + kBN == ct1) && (ct1 - 1 <= p_lo) &&
                               (ct1 - 1 < P || ct0 >= p_hi - W + 1);
-            tile_step<D, true>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, ct1, P, W, l16, lg, !full,
-                               grp_b, 1.f, 1.f);
+            tile_step_pinned<D>(st, qop, k_s[cur], v_s[cur], row_pos, ct0, ct1, P, W, l16, lg,
+                                !full, grp_b, __any(st.mb[0] != 0.f || st.mb[1] != 0.f));
             if (!grp_b) __syncthreads();
             if (!have) break;
             cseg = nseg;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
             *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * lg) = w;
         }
         if (lse != nullptr && lg == 0)
-            lse[((size_t)b * chunk + cl) * c.Hq + hq] = (st.m[rb] + __log2f(l)) * kLn2;
+            lse[((size_t)b * chunk + cl) * c.Hq + hq] = (st.mb[rb] + __log2f(l)) * kLn2;
     }
 }
 

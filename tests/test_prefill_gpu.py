@@ -128,3 +128,41 @@ def test_float32_storage_rejected():
         c.prefill(q, k, k.clone())
     assert e.value.status == psa.PSA_ERR_ARG
     assert c.seq_length(0) == 0
+
+
+@pytest.mark.parametrize("factor", [16.0, 64.0, -32.0])
+def test_large_logits(factor):
+    # Queries scaled by a power of two (exact in bf16): logits in the log2 domain reach far
+    # past +-64, so the softmax reference leaves 0 (a row's first visible tile takes its
+    # maximum, later tiles move it up and rescale O and l). Every value row of a sequence is
+    # the same vector, so each output row must equal it exactly whatever the weights (O and
+    # l rescaled alike), and lse must match the oracle within the key-rounding bound, which
+    # grows with |factor|.
+    W, C = 300, 128
+    prefix = [40, 0, 7]
+    n_hist = [900, 250, 20]
+    B, Hkv, D = 3, 8, 128
+    wl = configs.Workload("pf-big", torch.bfloat16, B, 16, Hkv, D, W, prefix, [1] * B, "prefill")
+    c = drive.make_cache(wl, max_chunk=C)
+    for b in range(B):
+        c.reset(b, prefix[b])
+    T = max(n_hist) + C
+    k_all, _ = drive.kv_block(wl, [0] * B, T, "cuda")
+    vrow = (torch.arange(B * Hkv * D, device="cuda").view(B, 1, Hkv, D) % 17 - 8).to(torch.bfloat16) / 4
+    v_all = vrow.expand(B, T, Hkv, D).contiguous()
+    c.append(k_all[:, :max(n_hist)].contiguous(), v_all[:, :max(n_hist)].contiguous(), n_new=n_hist)
+    q = drive.query_block(wl, n_hist, C, "cuda") * factor
+    kc = torch.stack([k_all[b, n_hist[b]:n_hist[b] + C] for b in range(B)]).contiguous()
+    vc = v_all[:, :C].contiguous()
+    lse = torch.empty((B, C, wl.n_q_heads), dtype=torch.float32, device="cuda")
+    out = c.prefill(q, kc, vc, lse=lse)
+    torch.cuda.synchronize()
+    want = vrow[:, 0].repeat_interleave(wl.n_q_heads // Hkv, dim=1)        # [B][Hq][D]
+    assert torch.equal(out, want.unsqueeze(1).expand_as(out)), "outputs differ from the constant value row"
+    lc, qc = lse.cpu().numpy(), q.double().cpu().numpy()
+    kd, vd = k_all.double().cpu().numpy(), v_all.double().cpu().numpy()
+    for b in range(B):
+        hist = attn.array_history(kd[b], vd[b])
+        _, ref_lse = attn.prefill_chunk(qc[b], n_hist[b], hist, prefix[b], W, Hkv, wl.rope_base,
+                                        wl.scale)
+        np.testing.assert_allclose(lc[b], ref_lse, rtol=0, atol=2e-2 * abs(factor))
