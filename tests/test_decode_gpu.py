@@ -128,3 +128,29 @@ def test_split_count_invariance():
         lses.append(lse.cpu().numpy())
     for x in lses[1:]:
         np.testing.assert_allclose(x, lses[0], rtol=0, atol=2e-5)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_window_of_one(dtype):
+    # W = 1: each query sees its pinned prefix and itself only; with P = 0 the output is the
+    # token's own value row exactly (a softmax over one key). Every step from the empty cache
+    # through the prefix and well past it, on the two-call path and the fused step.
+    W = 1
+    prefix = [0, 3, 5]
+    wl = configs.Workload("w1", dtype, 3, 8, 4, 64, W, prefix, [1] * 3, "decode")
+    caches = [drive.make_cache(wl) for _ in range(2)]
+    for c in caches:
+        for b in range(3):
+            c.reset(b, prefix[b])
+    for p in range(12):
+        k, v = drive.kv_block(wl, [p] * 3, 1, "cuda")
+        q = drive.queries(wl, [p] * 3, "cuda")
+        caches[0].append(k, v)
+        o2 = caches[0].decode(q)
+        of = caches[1].decode_step(k[:, 0].contiguous(), v[:, 0].contiguous(), q)
+        assert torch.equal(o2, of), f"step {p}"
+        assert torch.equal(o2[0], v[0, 0].repeat_interleave(2, dim=0)), f"P = 0, step {p}"
+        o, qc = o2.double().cpu().numpy(), q.double().cpu().numpy()
+        for b in range(3):
+            ref, _ = oracle_decode(wl, b, p, qc[b])
+            tol_check(o[b], ref, dtype, f"step {p} seq {b}")

@@ -166,3 +166,25 @@ def test_large_logits(factor):
         _, ref_lse = attn.prefill_chunk(qc[b], n_hist[b], hist, prefix[b], W, Hkv, wl.rope_base,
                                         wl.scale)
         np.testing.assert_allclose(lc[b], ref_lse, rtol=0, atol=2e-2 * abs(factor))
+
+
+def test_window_of_one_chunks():
+    # W = 1 with chunks: row c sees the prefix and itself; P = 0 gives the value rows exactly
+    W, C = 1, 40
+    prefix = [0, 6]
+    wl = configs.Workload("pf-w1", torch.bfloat16, 2, 16, 8, 128, W, prefix, [1, 1], "prefill")
+    c = drive.make_cache(wl, max_chunk=C)
+    for b in range(2):
+        c.reset(b, prefix[b])
+    n = [0, 0]
+    for _ in range(3):
+        q = drive.query_block(wl, n, C, "cuda")
+        k, v = drive.kv_block(wl, n, C, "cuda")
+        out = c.prefill(q, k, v)
+        assert torch.equal(out[0], v[0].repeat_interleave(2, dim=1))
+        n = [x + C for x in n]
+    n = [0, 0]
+    c2 = drive.make_cache(wl, max_chunk=C)
+    for b in range(2):
+        c2.reset(b, prefix[b])
+    run_chunk(c2, wl, n, C)
