@@ -397,7 +397,7 @@ FLAT_T = (2148, 4196, 8392, 32768, 131072)
 def bench_flat_in_t(warmup: int = 10, steps: int = 50):
     """The default decode shape (64 sequences, P = 100, W = 4096) at several t: the step
     must cost the same once the window is full ([PS] 04: per-step cost O((P + W) d),
-    independent of t). One cache is brought from one t to the next by appends."""
+    independent of t). Each t starts from a reset cache filled by appends."""
     import torch
 
     from synth import configs, drive
@@ -405,20 +405,11 @@ def bench_flat_in_t(warmup: int = 10, steps: int = 50):
     wl = configs.decode_p100_w4096()
     B = wl.batch
     c = drive.make_cache(wl)
-    res, n = {}, 0
+    res = {}
     for t in FLAT_T:
-        target = t - 1
-        if n == 0:
-            fill_timing(c, wl, [target] * B)
-        elif target > n:
-            k, v = drive.kv_block(wl, [0] * B, 4096, "cuda")
-            while n < target:
-                r = min(4096, target - n)
-                c.append(k, v, n_new=[r] * B)
-                n += r
-        n = target
-        ms, times, vis = time_steps(c, wl, [n] * B, warmup, steps)
-        n += warmup + 2 * steps
+        # every t from a freshly reset cache, as a separate run would see it
+        fill_timing(c, wl, [t - 1] * B)
+        ms, times, vis = time_steps(c, wl, [t - 1] * B, warmup, steps)
         res[str(t)] = {"us_per_step": ms * 1e3,
                        "decode_partial_us": times["decode_partial"][0] / times["decode_partial"][1] * 1e3,
                        "visible_per_sequence": vis[1] // B}
