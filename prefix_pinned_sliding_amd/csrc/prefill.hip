@@ -95,15 +95,22 @@ __global__ __launch_bounds__(1024) void stage_chunk_kernel(DevCache c, const uin
 // MFMA B operands of one 16-row block from a query row of the chunk: this lane's dims
 // 32 ks + 8 lg + j, rotated at position p (dim i < D / 2 pairs with i + D / 2, which the same
 // lane holds in k-step ks + KS / 2), multiplied by `sc` and rounded to bf16. `qrow` points
-// at the row's element 8 lg.
+// at the row's element 8 lg. fetch_query issues the row's 16-byte loads, rotate_query_ops
+// turns them into operands; load_query does both at once.
 template <int D>
-__device__ __forceinline__ void load_query(bf16x8 (&qo)[D / 32], const uint16_t* qrow, int p,
-                                           const double* inv_freq, int lg, float sc) {
+__device__ __forceinline__ void fetch_query(u32x4 (&raw)[D / 32], const uint16_t* qrow) {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) raw[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 32);
+}
+
+template <int D>
+__device__ __forceinline__ void rotate_query_ops(bf16x8 (&qo)[D / 32], const u32x4 (&raw)[D / 32],
+                                                 int p, const double* inv_freq, int lg, float sc) {
     constexpr int KS = D / 32, HS = KS / 2;
 #pragma unroll
     for (int ks = 0; ks < HS; ++ks) {
-        const u32x4 xw = *reinterpret_cast<const u32x4*>(qrow + ks * 32);
-        const u32x4 yw = *reinterpret_cast<const u32x4*>(qrow + (ks + HS) * 32);
+        const u32x4 xw = raw[ks];
+        const u32x4 yw = raw[ks + HS];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t xb = (j & 1) ? (xw[j / 2] & 0xFFFF0000u) : (xw[j / 2] << 16);
@@ -115,6 +122,14 @@ __device__ __forceinline__ void load_query(bf16x8 (&qo)[D / 32], const uint16_t*
             qo[ks + HS][j] = (__bf16)yr;
         }
     }
+}
+
+template <int D>
+__device__ __forceinline__ void load_query(bf16x8 (&qo)[D / 32], const uint16_t* qrow, int p,
+                                           const double* inv_freq, int lg, float sc) {
+    u32x4 raw[D / 32];
+    fetch_query<D>(raw, qrow);
+    rotate_query_ops<D>(qo, raw, p, inv_freq, lg, sc);
 }
 
 // The key ranges of a workgroup, in walk order: 0 = prefix in the cache, 1 = prefix
@@ -301,8 +316,12 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     // renumbered position, its index in the list [prefix, window] after the append
     // (p inside the prefix, else P + min(w_b, p + 1 - wfloor) - 1); the operands are
     // rotated again at p once the walk leaves the prefix.
+    // The query rows' loads go out first; they are rotated after the first key tile's loads
+    // have been issued, so that the rotation overlaps those loads.
     bool q_prefix = c.pe_mode == PSA_PE_RESET;
     const float q_sc = c.scale * kLog2e;
+    int q_pos[2];
+    u32x4 q_raw[2][KS];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int r = 32 * wave + 16 * rb + l16;
@@ -311,8 +330,8 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
         row_pos[rb] = n + c0 + r / G;
         q_off[rb] = (((size_t)b * chunk + cl) * c.Hq + h * G + g) * D + 8 * lg;
         const int p = n + cl;
-        const int pq = q_prefix && p >= c.pre[b] ? c.pre[b] + min(c.wlen[b], p + 1 - c.wfloor[b]) - 1 : p;
-        load_query<D>(qop[rb], q_in + q_off[rb], pq, c.inv_freq, lg, q_sc);
+        q_pos[rb] = q_prefix && p >= c.pre[b] ? c.pre[b] + min(c.wlen[b], p + 1 - c.wfloor[b]) - 1 : p;
+        fetch_query<D>(q_raw[rb], q_in + q_off[rb]);
     }
 
     SoftmaxRows<DB> st;
@@ -367,6 +386,9 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
         stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
         bool have = walk_next<kBN>(wk, seg, t0, t1);
         if (have) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            rotate_query_ops<D>(qop[rb], q_raw[rb], q_pos[rb], c.inv_freq, lg, q_sc);
         __syncthreads();
 #pragma unroll 1
         while (true) {
