@@ -394,30 +394,44 @@ def bench_decode_config(name: str, warmup: int, steps: int):
 FLAT_T = (2148, 4196, 8392, 32768, 131072)
 
 
-def bench_flat_in_t(warmup: int = 10, steps: int = 50):
+def bench_flat_in_t(warmup: int = 10, steps: int = 50, rounds: int = 3):
     """The default decode shape (64 sequences, P = 100, W = 4096) at several t: the step
     must cost the same once the window is full ([PS] 04: per-step cost O((P + W) d),
-    independent of t). Each t starts from a reset cache filled by appends."""
+    independent of t). Each t has its own cache, reset and filled by appends; the t values
+    are timed in interleaved rounds (t1, t2, ..., t1, t2, ...), so that a change of clock
+    during the sweep falls on every t alike, and each t reports the median of its rounds."""
     import torch
 
     from synth import configs, drive
 
     wl = configs.decode_p100_w4096()
     B = wl.batch
-    c = drive.make_cache(wl)
+    state = {}
+    for t in FLAT_T:
+        c = drive.make_cache(wl)
+        fill_timing(c, wl, [t - 1] * B)
+        state[t] = [c, t - 1]
+    runs = {t: [] for t in FLAT_T}
+    for _ in range(rounds):
+        for t in FLAT_T:
+            c, n = state[t]
+            ms, times, vis = time_steps(c, wl, [n] * B, warmup, steps)
+            state[t][1] = n + warmup + 2 * steps
+            runs[t].append((ms * 1e3, times["decode_partial"][0] / times["decode_partial"][1] * 1e3,
+                            vis[1] // B))
+    del state, c
+    torch.cuda.empty_cache()
     res = {}
     for t in FLAT_T:
-        # every t from a freshly reset cache, as a separate run would see it
-        fill_timing(c, wl, [t - 1] * B)
-        ms, times, vis = time_steps(c, wl, [t - 1] * B, warmup, steps)
-        res[str(t)] = {"us_per_step": ms * 1e3,
-                       "decode_partial_us": times["decode_partial"][0] / times["decode_partial"][1] * 1e3,
-                       "visible_per_sequence": vis[1] // B}
-    del c
-    torch.cuda.empty_cache()
+        step_us = sorted(r[0] for r in runs[t])
+        part_us = sorted(r[1] for r in runs[t])
+        res[str(t)] = {"us_per_step": step_us[len(step_us) // 2],
+                       "decode_partial_us": part_us[len(part_us) // 2],
+                       "us_per_step_rounds": [r[0] for r in runs[t]],
+                       "visible_per_sequence": runs[t][-1][2]}
     full = [res[str(t)]["us_per_step"] for t in FLAT_T if t >= 4196]
     return {"workload": "decode-bf16-B64-P100-W4096 at several t", "warmup": warmup,
-            "steps": steps, "t": res,
+            "steps": steps, "rounds": rounds, "t": res,
             "spread_full_window": (max(full) - min(full)) / (sum(full) / len(full))}
 
 
