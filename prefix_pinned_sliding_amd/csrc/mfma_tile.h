@@ -244,7 +244,9 @@ __device__ __forceinline__ bool tile_max_pinned(f32x4 (&s)[2][kTileKeys / 16],
             const bool first = st.m[rb] == kNeg;
             const float nb = first && mt <= kRefRange && mt >= -kRefRange ? 0.f : mt;
             if (nb != st.mb[rb]) {
-                const float f = __builtin_amdgcn_exp2f(st.mb[rb] - nb);
+                // on the row's first visible keys O and l are still zero: the factor is not
+                // formed (for a maximum below -128 it would overflow, and 0 * inf is NaN)
+                const float f = first ? 0.f : __builtin_amdgcn_exp2f(st.mb[rb] - nb);
                 const float shift = nb - st.mb[rb];
                 st.l[rb] *= f;
 #pragma unroll

@@ -168,6 +168,51 @@ def test_large_logits(factor):
         np.testing.assert_allclose(lc[b], ref_lse, rtol=0, atol=2e-2 * abs(factor))
 
 
+def test_first_keys_far_below_zero():
+    # Every logit is about -261 in the log2 domain: keys carry all their energy in the
+    # lowest-frequency rotation pair (dims D/2 - 1 and D - 1, turned by less than 0.04 rad over
+    # these positions) and queries point the other way. A row's first visible tile then takes
+    # its maximum as the softmax reference while O and l are still zero; forming the rescale
+    # factor 2^261 there would overflow and turn them into NaN. The logits of a row differ by
+    # less than 0.1 (log2) from key to key, about what rounding the rotated keys to bf16 moves
+    # them, so the weights are not compared: every value row of a sequence is the same
+    # vector, and each output row must equal it exactly. lse against the oracle within the
+    # rounding of the two nonzero components of the rotated, scaled query (|q_i| < 17, bf16
+    # error <= 1/16) and of the rotated key (|k_i| < 8.5, error <= 1/32):
+    # 2 (8.5 / 16 + 17 / 32) = 2.1 in log2, 1.47 in natural log.
+    W, C = 64, 96
+    prefix = [5, 0]
+    n_hist = [150, 40]
+    B, Hkv, Hq, D = 2, 8, 16, 128
+    wl = configs.Workload("pf-neg", torch.bfloat16, B, Hq, Hkv, D, W, prefix, [1] * B, "prefill")
+    c = drive.make_cache(wl, max_chunk=C)
+    for b in range(B):
+        c.reset(b, prefix[b])
+    T = max(n_hist) + C
+    u = torch.zeros(D)
+    u[D // 2 - 1] = 8.0
+    u[D - 1] = 8.0
+    k_all = u.to(torch.bfloat16).view(1, 1, 1, D).expand(B, T, Hkv, D).contiguous().cuda()
+    vrow = (torch.arange(B * Hkv * D, device="cuda").view(B, 1, Hkv, D) % 13 - 6).to(torch.bfloat16) / 8
+    v_all = vrow.expand(B, T, Hkv, D).contiguous()
+    c.append(k_all[:, :max(n_hist)].contiguous(), v_all[:, :max(n_hist)].contiguous(), n_new=n_hist)
+    q = (-16.0 * u).to(torch.bfloat16).view(1, 1, 1, D).expand(B, C, Hq, D).contiguous().cuda()
+    kc = torch.stack([k_all[b, n_hist[b]:n_hist[b] + C] for b in range(B)]).contiguous()
+    vc = v_all[:, :C].contiguous()
+    lse = torch.empty((B, C, Hq), dtype=torch.float32, device="cuda")
+    out = c.prefill(q, kc, vc, lse=lse)
+    torch.cuda.synchronize()
+    want = vrow[:, 0].repeat_interleave(Hq // Hkv, dim=1)        # [B][Hq][D]
+    assert torch.equal(out, want.unsqueeze(1).expand_as(out)), "outputs differ from the constant value row"
+    lc = lse.cpu().numpy()
+    kd, vd, qd = k_all.double().cpu().numpy(), v_all.double().cpu().numpy(), q.double().cpu().numpy()
+    for b in range(B):
+        _, ref_lse = attn.prefill_chunk(qd[b], n_hist[b], attn.array_history(kd[b], vd[b]),
+                                        prefix[b], W, Hkv, wl.rope_base, wl.scale)
+        assert ref_lse.max() < -128 * np.log(2), "the workload must reach past the overflow"
+        np.testing.assert_allclose(lc[b], ref_lse, rtol=0, atol=1.47)
+
+
 def test_window_of_one_chunks():
     # W = 1 with chunks: row c sees the prefix and itself; P = 0 gives the value rows exactly
     W, C = 1, 40
