@@ -153,15 +153,19 @@ __device__ __forceinline__ bool tile_max(f32x4 (&s)[2][kTileKeys / 16],
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         if (masked) {
+            // key j = jb + c (c = 16 kb + i) is visible iff c <= hi and c is not in the gap
+            // [pe, pe + gap) between the prefix and the window
             const int p = row_pos[rb];
             int jb = ct0 + 4 * lg;
             asm volatile("" : "+v"(jb));   // keeps the mask's arithmetic inside this branch
+            const int hi = min(p, t1 - 1) - jb, pe = P - jb;
+            const unsigned gap = (unsigned)max(p - W + 1 - P, 0);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int j = jb + kb * 16 + i;
-                    const bool vis = j < t1 && j <= p && (j < P || j >= p - W + 1);
+                    const int cc = kb * 16 + i;
+                    const bool vis = cc <= hi && (unsigned)(cc - pe) >= gap;
                     s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
                 }
         }

@@ -43,10 +43,6 @@ struct TrainArgs {
     float scale;
 };
 
-__device__ __forceinline__ bool visible(int i, int j, int P, int W) {
-    return j <= i && (j < P || j >= i - W + 1);
-}
-
 // XCD-aware order: workgroup L runs on XCD L % 8; consecutive logical tiles (those of one
 // (sequence, KV head)) go to one XCD so the operands they share stay in its L2.
 __device__ __forceinline__ int xcd_logical(int total) {
@@ -398,12 +394,25 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
             lsq[rb] = *reinterpret_cast<const float4*>(&lse_s[buf][rb * 16 + 4 * lg]);
             dsq[rb] = *reinterpret_cast<const float4*>(&di_s[buf][rb * 16 + 4 * lg]);
         }
+        if (!full) {
+            // invisible products to -inf (then P = exp2(-inf) = 0): row r of the step is at
+            // position i0 + r / G; this lane's key is seen by positions [key, key + W - 1]
+            // (every later one for a prefix key), by valid rows only
+            const int d0 = i0 - key;
+            const unsigned span = key < P ? 0x7fffffffu : (unsigned)(W - 1);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rb * 16 + 4 * lg + i;
+                    const bool vis = r <= last && key < k1 && (unsigned)(d0 + r / G) <= span;
+                    s[rb][i] = vis ? s[rb][i] : -INFINITY;
+                }
+        }
         auto pds = [&](int rb, int i) {   // P and dS of row 16 rb + 4 lg + i
             const float ls = i == 0 ? lsq[rb].x : (i == 1 ? lsq[rb].y : (i == 2 ? lsq[rb].z : lsq[rb].w));
             const float ds = i == 0 ? dsq[rb].x : (i == 1 ? dsq[rb].y : (i == 2 ? dsq[rb].z : dsq[rb].w));
-            const int r = rb * 16 + 4 * lg + i;
-            const bool vis = full || (r <= last && key < k1 && visible(i0 + r / G, key, P, W));
-            const float p = vis ? __builtin_amdgcn_exp2f(s[rb][i] * sc - ls) : 0.f;
+            const float p = __builtin_amdgcn_exp2f(s[rb][i] * sc - ls);
             const float d = p * (dp[rb][i] - ds);
             pa[rb / 2][(rb & 1) * 4 + i] = (__bf16)p;
             sa[rb / 2][(rb & 1) * 4 + i] = (__bf16)d;
@@ -565,6 +574,26 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
             }
         }
         // dS^T as B operands (k = keys in vt_col order)
+        if (!full) {
+            // invisible products to -inf (then P = exp2(-inf) = 0): key jb + c (c = 16 kb + i)
+            // is visible iff c <= hi and c is not in the gap [pe, pe + gap) between the prefix
+            // and the window
+            const int jb = ct0 + 4 * lg;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int p = row_pos[rb];
+                const int hi = min(p, t1 - 1) - jb, pe = P - jb;
+                const unsigned gap = (unsigned)max(p - W + 1 - P, 0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int cc = kb * 16 + i;
+                        const bool vis = cc <= hi && (unsigned)(cc - pe) >= gap;
+                        s[rb][kb][i] = vis ? s[rb][kb][i] : -INFINITY;
+                    }
+            }
+        }
         bf16x8 sb[2][PVS];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -572,9 +601,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int j = ct0 + kb * 16 + 4 * lg + i;
-                    const bool vis = full || (j < t1 && visible(row_pos[rb], j, P, W));
-                    const float p = vis ? __builtin_amdgcn_exp2f(s[rb][kb][i] * sc - lse2[rb]) : 0.f;
+                    const float p = __builtin_amdgcn_exp2f(s[rb][kb][i] * sc - lse2[rb]);
                     sb[rb][kb / 2][(kb & 1) * 4 + i] = (__bf16)(p * (dp[rb][kb][i] - di[rb]));
                 }
         // dQ^T += K^T dS^T
