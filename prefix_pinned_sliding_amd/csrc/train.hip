@@ -326,18 +326,43 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
     const uint32_t g_lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&g_s[0][0]));
     float lse_r = 0.f, di_r = 0.f;
-    auto issue = [&](int i0, int buf) {
-        constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBR / RPL / kWaves;
-        static_assert(NPW * RPL * kWaves == kBR, "tile rows per wave");
-        const int last = (min(i0 + BP, len) - i0) * G - 1;
+    constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBR / RPL / kWaves;
+    static_assert(NPW * RPL * kWaves == kBR, "tile rows per wave");
+    // row r of a step (position r / G, head r % G) starts ((r / G) Hq + r % G) D elements
+    // after the step's first row; its chunks land swizzled by r. This lane's rows of a full
+    // step, once: r = (NPW wave + x) RPL + lane / CPR.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto lane_off = [&](int r, int src) {
+        return (uint32_t)(((src / G) * a.Hq + src % G) * D + ((lane % CPR) ^ chunk_swz<D>(r)) * 8);
+    };
+    uint32_t loff[NPW];
 #pragma unroll
-        for (int x = 0; x < NPW; ++x) {
-            const int blk = wave * NPW + x;
-            const int r = blk * RPL + lane / CPR;
-            const size_t e = row_off(i0, min(r, last)) + ((lane % CPR) ^ chunk_swz<D>(r)) * 8;
-            const uint32_t o = (uint32_t)(buf * kBR * D * 2 + blk * 1024);
-            lds_dma16(q_lds + o, a.q + e);
-            lds_dma16(g_lds + o, a.dout + e);
+    for (int x = 0; x < NPW; ++x) {
+        const int r = (wave_u * NPW + x) * RPL + lane / CPR;
+        loff[x] = lane_off(r, r);
+    }
+    auto issue = [&](int i0, int buf) {
+        const int last = (min(i0 + BP, len) - i0) * G - 1;
+        const size_t base = (row0 + (size_t)i0 * a.Hq) * D;
+        const uint16_t* qb = a.q + base;
+        const uint16_t* gb = a.dout + base;
+        if (last >= kBR - 1) {
+#pragma unroll
+            for (int x = 0; x < NPW; ++x) {
+                const uint32_t o = (uint32_t)(buf * kBR * D * 2 + (wave_u * NPW + x) * 1024);
+                lds_dma16(q_lds + o, qb + loff[x]);
+                lds_dma16(g_lds + o, gb + loff[x]);
+            }
+        } else {
+            // a short last step: rows past `last` repeat row `last`
+#pragma unroll
+            for (int x = 0; x < NPW; ++x) {
+                const int r = (wave_u * NPW + x) * RPL + lane / CPR;
+                const uint32_t e = lane_off(r, min(r, last));
+                const uint32_t o = (uint32_t)(buf * kBR * D * 2 + (wave_u * NPW + x) * 1024);
+                lds_dma16(q_lds + o, qb + e);
+                lds_dma16(g_lds + o, gb + e);
+            }
         }
         if (tid < kBR) {
             const size_t ri = row_off(i0, min(tid, last)) / D;
@@ -517,19 +542,42 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&k_s[0][0]));
     const uint32_t v_lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&v_s[0][0]));
-    auto issue = [&](int sg, int s0, int buf) {
-        constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBN / RPL / kWaves;
-        static_assert(NPW * RPL * kWaves == kBN, "tile rows per wave");
-        const int last = min(s0 + kBN, sg == 0 ? wk.hi0 : wk.hi1) - 1 - s0;
+    constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBN / RPL / kWaves;
+    static_assert(NPW * RPL * kWaves == kBN, "tile rows per wave");
+    // key row r of a tile starts r Hkv D elements after the tile's first row; its chunks land
+    // swizzled by r. This lane's rows of a full tile, once: r = (NPW wave + x) RPL + lane / CPR.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto lane_off = [&](int r, int src) {
+        return (uint32_t)(src * a.Hkv * D + ((lane % CPR) ^ chunk_swz<D>(r)) * 8);
+    };
+    uint32_t loff[NPW];
 #pragma unroll
-        for (int x = 0; x < NPW; ++x) {
-            const int blk = wave * NPW + x;
-            const int r = blk * RPL + lane / CPR;
-            const size_t e = (kv0 + (size_t)(s0 + min(r, last)) * a.Hkv) * D +
-                             ((lane % CPR) ^ chunk_swz<D>(r)) * 8;
-            const uint32_t o = (uint32_t)(buf * kBN * D * 2 + blk * 1024);
-            lds_dma16(k_lds + o, a.k + e);
-            lds_dma16(v_lds + o, a.v + e);
+    for (int x = 0; x < NPW; ++x) {
+        const int r = (wave_u * NPW + x) * RPL + lane / CPR;
+        loff[x] = lane_off(r, r);
+    }
+    auto issue = [&](int sg, int s0, int buf) {
+        const int last = min(s0 + kBN, sg == 0 ? wk.hi0 : wk.hi1) - 1 - s0;
+        const size_t base = (kv0 + (size_t)s0 * a.Hkv) * D;
+        const uint16_t* kb_ = a.k + base;
+        const uint16_t* vb_ = a.v + base;
+        if (last >= kBN - 1) {
+#pragma unroll
+            for (int x = 0; x < NPW; ++x) {
+                const uint32_t o = (uint32_t)(buf * kBN * D * 2 + (wave_u * NPW + x) * 1024);
+                lds_dma16(k_lds + o, kb_ + loff[x]);
+                lds_dma16(v_lds + o, vb_ + loff[x]);
+            }
+        } else {
+            // a partial tile: rows past `last` repeat row `last`
+#pragma unroll
+            for (int x = 0; x < NPW; ++x) {
+                const int r = (wave_u * NPW + x) * RPL + lane / CPR;
+                const uint32_t e = lane_off(r, min(r, last));
+                const uint32_t o = (uint32_t)(buf * kBN * D * 2 + (wave_u * NPW + x) * 1024);
+                lds_dma16(k_lds + o, kb_ + e);
+                lds_dma16(v_lds + o, vb_ + e);
+            }
         }
     };
     // this lane's chunk swizzles: row reads (rows = l16 mod 16) and transposing reads
