@@ -226,13 +226,18 @@ int auto_split_tokens(psa_cache* c) {
         // Each sequence's last split is partial, so pieces of the mean length add up to
         // more than two rounds (half a workgroup per sequence on average). Lengthen the
         // splits to the shortest that keeps the grid within two full rounds (the count
-        // only falls as L grows, so a bisection finds it).
+        // only falls as L grows, so a bisection finds it). With Reset PE the prefix forms
+        // splits of its own, usually far shorter than L: they fill the gaps between the
+        // window splits and are not counted (counting them would push L up to where the
+        // window splits alone take more than two rounds).
         const int64_t budget = 2 * (int64_t)c->resident_wgs;
+        const bool reset = c->desc.pe_mode == PSA_PE_RESET;
         auto wgs = [&](int64_t len) {
             int64_t n = 0;
             for (int b = 0; b < c->desc.max_batch; ++b) {
                 const psa::SeqView v = view_of(c, b);
-                n += psa::split_count(v.n_pre, v.n_win, (int)len, c->desc.pe_mode);
+                n += reset ? (v.n_win + len - 1) / len
+                           : psa::split_count(v.n_pre, v.n_win, (int)len, c->desc.pe_mode);
             }
             return n * c->desc.n_kv_heads;
         };
