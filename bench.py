@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--prefill-calls", type=int, default=30)
+    ap.add_argument("--prefill-calls", type=int, default=100)
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--train-calls", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true",
@@ -171,11 +171,13 @@ def cpu_baseline(wl, n_now, q_rows, budget_s: float):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_prefill(calls: int, warmup: int = 2):
+def bench_prefill(calls: int, warmup: int = 20):
     """Chunked prefill: 8 sequences each take a 512-token chunk at t ~ U{8192..65536}.
 
     Each call attends the chunk (staging, MFMA attention) and appends it; the state
-    advances by 512 tokens per call. Algorithmic work per call: 4 * H_q * D * sum over
+    advances by 512 tokens per call. `warmup` untimed calls first bring the GPU to its
+    steady clocks (a call takes about 0.2 ms), then `calls` timed ones and `calls` more with
+    per-kernel events. Algorithmic work per call: 4 * H_q * D * sum over
     the chunk's queries of |A(p)| flops (QK^T and PV over the visible set).
     """
     import torch
