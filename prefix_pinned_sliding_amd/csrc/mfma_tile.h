@@ -26,10 +26,31 @@ __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kRescaleSlack = 8.0f;
 
 constexpr int kTileKeys = 64;           // keys per attention tile
-// LDS row strides (elements): K rows are read 16 bytes per lane, 8 rows per 128 bytes, so
-// a 4-bank offset between rows (D + 8) keeps them apart; V is read with transposing 8-byte
-// loads that take 4 rows x 32 bytes at once, which needs an 8-bank offset (D + 16).
-constexpr int kKPad = 8, kVPad = 16;
+// LDS row stride of V tiles (elements): V is read only with transposing 8-byte loads that
+// take 4 rows x 32 bytes at once, and an 8-bank offset between rows (D + 16) keeps them
+// apart. K tiles (and every tile read as 16-byte row operands) are unpadded and swizzled
+// (chunk_swz).
+constexpr int kVPad = 16;
+
+// Unpadded LDS tiles: the 16-byte chunk c of row r is stored at chunk c ^ chunk_swz<D>(r).
+// Measured on gfx950 with single-pattern probes: a 16-byte LDS read (ds_read_b128) is
+// served in four groups of 16 lanes, each group the lanes that share lane bit 5 and the
+// parity of lane bits 2..4; it runs at full rate (about 215 B/clk per CU) when the 16 lanes
+// of each group hit 16 distinct 16-byte bank groups (address bits 4..7), and at half rate
+// when two share one. A transposing 8-byte read (ds_read_b64_tr_b16) runs at its full rate
+// (about 150 B/clk) when each half of the wave (lanes 0..31, 32..63) hits 32 distinct
+// 8-byte slots of the 256-byte bank cycle. The row-operand reads (lane (l16, lg) of a
+// 16-row block: row l16, chunk 4 ks + lg) and the transposing reads (rows 4 lg + l16 / 4,
+// a chunk pair) both meet those conditions with c ^ 2 (r & 7) for 256-byte rows (D = 128)
+// and c ^ (r & 6) for 128-byte rows (D = 64). Padded rows (stride D + 8) and the XOR with
+// r & 15 put two lanes of a group on one bank group (half rate) for the row reads; r & 15
+// also halves the transposing reads.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+    static_assert(D == 64 || D == 128, "head dims 64 and 128");
+    if constexpr (D == 128) return (2 * r) & 14;
+    else return r & 6;
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) {
     return __builtin_bit_cast(bf16x8, w);
@@ -70,9 +91,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// Registers -> LDS: K and V rows as they are (consecutive lanes on consecutive 16-byte
-// chunks of a row); V^T operands are read back with transposing LDS loads.
-template <int D, int BN, int NT, int KSTR, int VSTR>
+// Registers -> LDS (consecutive lanes on consecutive 16-byte chunks of a row): K rows
+// unpadded with their chunks swizzled (chunk_swz), V rows padded to VSTR; V^T operands
+// are read back with transposing LDS loads.
+template <int D, int BN, int NT, int VSTR>
 __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* v_s, int tid,
                                            const u32x4* kreg, const u32x4* vreg) {
     constexpr int CPR = D / 8;
@@ -81,9 +103,18 @@ __device__ __forceinline__ void stage_tile(uint16_t* k_s, uint16_t* v_s, int tid
     for (int rr = 0; rr < KLD; ++rr) {
         const int ci = tid + NT * rr;
         const int kk = ci / CPR, col = ci % CPR;
-        *reinterpret_cast<u32x4*>(k_s + kk * KSTR + col * 8) = kreg[rr];
+        *reinterpret_cast<u32x4*>(k_s + kk * D + (col ^ chunk_swz<D>(kk)) * 8) = kreg[rr];
         *reinterpret_cast<u32x4*>(v_s + kk * VSTR + col * 8) = vreg[rr];
     }
+}
+
+// This lane's K operand offsets within a 16-row block (elements, from the block's first
+// row): row l16, chunk 4 ks + lg, swizzled, for each k-step ks.
+template <int D>
+__device__ __forceinline__ void k_operand_offsets(int (&ko)[D / 32], int l16, int lg) {
+    const int swz = chunk_swz<D>(l16);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) ko[ks] = l16 * D + ((4 * ks + lg) ^ swz) * 8;
 }
 
 // Online-softmax state of one lane's two row blocks. m: running maximum (log2 domain),
@@ -112,7 +143,6 @@ __device__ __forceinline__ void tile_qk(f32x4 (&s)[2][kTileKeys / 16], const Sof
                                         const bf16x8 (&qop)[2][D / 32], const uint16_t* k_s,
                                         int l16, int lg, float inv_sc) {
     constexpr int KS = D / 32, KB = kTileKeys / 16;
-    constexpr int KSTR = D + kKPad;
     const float s0 = -st.mb[0] * inv_sc, s1 = -st.mb[1] * inv_sc;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -121,18 +151,19 @@ __device__ __forceinline__ void tile_qk(f32x4 (&s)[2][kTileKeys / 16], const Sof
     }
     // k-step outer: the 8 accumulators are independent within a step, and the next step's
     // K operands are read while this step's products run
+    int ko[KS];
+    k_operand_offsets<D>(ko, l16, lg);
     bf16x8 ka[2][KB];
-    const uint16_t* kp = k_s + l16 * KSTR + 8 * lg;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-        ka[0][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kb * 16 * KSTR));
+        ka[0][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(k_s + kb * 16 * D + ko[0]));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 ka[(ks + 1) & 1][kb] = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(kp + kb * 16 * KSTR + (ks + 1) * 32));
+                    *reinterpret_cast<const u32x4*>(k_s + kb * 16 * D + ko[ks + 1]));
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -336,7 +367,6 @@ __device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x
                                             const bf16x8 (&qop)[2][D / 32], const uint16_t* k_s,
                                             int l16, int lg, float sc, float inv_sc) {
     constexpr int KS = D / 32, KB = kTileKeys / 16;
-    constexpr int KSTR = D + kKPad;
     static_assert(KB == 4 && 16 % KS == 0, "two halves of two 16-key blocks");
     // ZERO: every row of the wave has reference 0, so the accumulators start from the
     // products' inline constant 0 instead of 32 register moves
@@ -350,10 +380,11 @@ __device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x
     // one step ahead
     constexpr int NS = 2 * KS;
     bf16x8 ka[2][2];
-    const uint16_t* kp = k_s + l16 * KSTR + 8 * lg;
+    int ko[KS];
+    k_operand_offsets<D>(ko, l16, lg);
     auto kread = [&](int step, int j) -> bf16x8 {
         const int h = step / KS, ks = step % KS;
-        return as_bf16x8(*reinterpret_cast<const u32x4*>(kp + (2 * h + j) * 16 * KSTR + ks * 32));
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(k_s + (2 * h + j) * 16 * D + ko[ks]));
     };
     ka[0][0] = kread(0, 0);
     ka[0][1] = kread(0, 1);

@@ -276,12 +276,11 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     constexpr int DB = D / 16;            // d-blocks of O^T
     constexpr int KB = kBN / 16;          // key blocks per tile
     constexpr int PVS = kBN / 32;         // k-steps of O^T = V^T P^T
-    constexpr int KSTR = D + kKPad;       // LDS row strides (elements)
     constexpr int VSTR = D + kVPad;
     constexpr int CPR = D / 8;            // 16-byte chunks per row
     constexpr int KLD = (kBN * CPR) / kPfBlock;
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[kNBuf][kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[kNBuf][kBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t v_s[kNBuf][kBN * VSTR];
 
     // XCD-aware tile order: workgroup L runs on XCD L % 8; give each XCD a contiguous run
@@ -383,7 +382,7 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
     if (walk_next<kBN>(wk, seg, t0, t1)) {
         int cseg = seg, ct0 = t0, ct1 = t1, cur = 0;
         fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
-        stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
+        stage_tile<D, kBN, kPfBlock, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
         bool have = walk_next<kBN>(wk, seg, t0, t1);
         if (have) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
 #pragma unroll
@@ -396,7 +395,7 @@ __global__ __launch_bounds__(kPfBlock, 1) void prefill_kernel(DevCache c, const 
             const int nxt = cur == 2 ? 0 : cur + 1;
             bool have_next = false;
             if (have) {
-                stage_tile<D, kBN, kPfBlock, KSTR, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
+                stage_tile<D, kBN, kPfBlock, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
                 have_next = walk_next<kBN>(wk, seg, t0, t1);
                 if (have_next) fetch_tile<D, kBN, kPfBlock, PAGED>(src, seg, t0, t1, tid, kreg, vreg);
             }

@@ -97,9 +97,9 @@ template <int D, int G>
 __global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, int n_qtiles) {
     constexpr int BQ = kFwdRows / G;
     constexpr int KS = D / 32, DB = D / 16;
-    constexpr int KSTR = D + kKPad, VSTR = D + kVPad;
+    constexpr int VSTR = D + kVPad;
     constexpr int KLD = (kTileKeys * (D / 8)) / kFwdBlock;
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[3][kTileKeys * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[3][kTileKeys * D];
     __shared__ __attribute__((aligned(16))) uint16_t v_s[3][kTileKeys * VSTR];
 
     const int total = n_qtiles * a.Hkv * a.B;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, in
     if (wk.next(seg, t0)) {
         int ct0 = t0, chi = seg_hi(seg), cur = 0;
         fetch_rows<D>(a, kv0, t0, min(t0 + kTileKeys, chi) - 1 - t0, tid, kreg, vreg);
-        stage_tile<D, kTileKeys, kFwdBlock, KSTR, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
+        stage_tile<D, kTileKeys, kFwdBlock, VSTR>(k_s[0], v_s[0], tid, kreg, vreg);
         bool have = wk.next(seg, t0);
         if (have) fetch_rows<D>(a, kv0, t0, min(t0 + kTileKeys, seg_hi(seg)) - 1 - t0, tid, kreg, vreg);
         __syncthreads();
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, in
             const int nxt = cur == 2 ? 0 : cur + 1;
             bool have_next = false;
             if (have) {
-                stage_tile<D, kTileKeys, kFwdBlock, KSTR, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
+                stage_tile<D, kTileKeys, kFwdBlock, VSTR>(k_s[nxt], v_s[nxt], tid, kreg, vreg);
                 have_next = wk.next(seg, t0);
                 if (have_next)
                     fetch_rows<D>(a, kv0, t0, min(t0 + kTileKeys, seg_hi(seg)) - 1 - t0, tid, kreg, vreg);
@@ -225,23 +225,6 @@ __global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
     a.di[idx] = acc;
 }
 
-// Unpadded LDS tiles with the 16-byte chunk c of row r stored at chunk c ^ chunk_swz<D>(r),
-// a function of r mod 16. The reads: 16-byte row reads (16 lanes on 16 consecutive rows, one
-// logical chunk each) and transposing 8-byte reads (each 16-lane group takes a chunk pair
-// from 4 consecutive rows). The swizzle puts every such read on distinct banks whether the
-// LDS serves 16-byte reads 8 lanes at a time from 32 four-byte banks (and 8-byte reads 16 at
-// a time), or 16 lanes at a time from 64 banks (8-byte reads 32 at a time): for D = 128
-// (256-byte rows) it is a permutation of 0 .. 15 on rows 0 .. 15, a permutation of 0 .. 7
-// modulo 8 on rows 0 .. 7 and on 8 .. 15, and its half is distinct modulo 8 on each 8-row
-// half and modulo 4 on each 4-row quarter; for D = 64 (128-byte rows, two per 256 bytes) the
-// same holds on the even and the odd rows separately. (An 8-row swizzle leaves rows r and
-// r + 8 on the same banks when 64 banks serve 16 lanes.)
-template <int D>
-__device__ __forceinline__ int chunk_swz(int r) {
-    const int b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
-    if constexpr (D == 128) return 2 * (r & 3) + (b2 ^ b3) + 8 * b2;
-    else return ((5 * (r & 7)) ^ b3) & 7;
-}
 
 // One wave-wide direct load into LDS: lane l's 16 bytes at `g` land at LDS byte address
 // lds + 16 l (global_load_lds_dwordx4, LDS base in M0). The compiler does not see this
