@@ -234,9 +234,15 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, const void* g) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
 }
+// At most N vector-memory loads in flight. The builtin (not inline assembly) lets the
+// compiler's own wait placement see it: after lds_dma_wait<0>() it knows every earlier load
+// has landed on every path, and adds no waits for them later in the loop (such waits would
+// also wait for the next step's direct loads, which it cannot see).
 template <int N>
-__device__ __forceinline__ void lds_dma_wait() {   // at most N vector-memory loads in flight
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+__device__ __forceinline__ void lds_dma_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -246,9 +252,11 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int n_ktiles) {
     constexpr int BP = kBR / G;                 // positions per query step
     constexpr int KS = D / 32, DB = D / 16, RB = kBR / 16, RS = kBR / 32;
-    // Q and dO tiles: two buffers each, unpadded rows with chunk_swz, filled by direct loads
-    __shared__ __attribute__((aligned(1024))) uint16_t q_s[2][kBR * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t g_s[2][kBR * D];
+    // Q and dO tiles: two buffers, each the Q tile then the dO tile (one base address serves
+    // both, the dO reads at a fixed offset); unpadded rows with chunk_swz, filled by direct
+    // loads
+    constexpr int TB = kBR * D * 2;             // bytes of one tile
+    __shared__ __attribute__((aligned(1024))) uint16_t qg_s[2][2 * kBR * D];
     __shared__ __attribute__((aligned(16))) float lse_s[2][kBR];
     __shared__ __attribute__((aligned(16))) float di_s[2][kBR];
 
@@ -305,9 +313,8 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
     // its share; the loads are waited for at the top of that step), its lse and D rows
     // into registers; both one step ahead of the products.
     const uint32_t q_lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&q_s[0][0]));
-    const uint32_t g_lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&g_s[0][0]));
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&qg_s[0][0]));
+    const uint32_t g_lds = q_lds + TB;
     float lse_r = 0.f, di_r = 0.f;
     constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBR / RPL / kWaves;
     static_assert(NPW * RPL * kWaves == kBR, "tile rows per wave");
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         if (last >= kBR - 1) {
 #pragma unroll
             for (int x = 0; x < NPW; ++x) {
-                const uint32_t o = (uint32_t)(buf * kBR * D * 2 + (wave_u * NPW + x) * 1024);
+                const uint32_t o = (uint32_t)(buf * 2 * TB + (wave_u * NPW + x) * 1024);
                 lds_dma16(q_lds + o, qb + loff[x]);
                 lds_dma16(g_lds + o, gb + loff[x]);
             }
@@ -342,14 +349,14 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
             for (int x = 0; x < NPW; ++x) {
                 const int r = (wave_u * NPW + x) * RPL + lane / CPR;
                 const uint32_t e = lane_off(r, min(r, last));
-                const uint32_t o = (uint32_t)(buf * kBR * D * 2 + (wave_u * NPW + x) * 1024);
+                const uint32_t o = (uint32_t)(buf * 2 * TB + (wave_u * NPW + x) * 1024);
                 lds_dma16(q_lds + o, qb + e);
                 lds_dma16(g_lds + o, gb + e);
             }
         }
         if (tid < kBR) {
             const size_t ri = row_off(i0, min(tid, last)) / D;
-            lse_r = a.lse[ri] * kLog2e;
+            lse_r = a.lse[ri];   // scaled when stored: a use here would wait for every load
             di_r = a.di[ri];
         }
     };
@@ -366,30 +373,52 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
                           (k1 - 1 < P || k0 >= (i1 - 1) - W + 1);
         lds_dma_wait<0>();
         if (tid < kBR) {
-            lse_s[buf][tid] = lse_r;
+            lse_s[buf][tid] = lse_r * kLog2e;
             di_s[buf][tid] = di_r;
         }
         // step i0's tiles are in place, and every wave is done with the other buffer
         __syncthreads();
         if (i0 + BP < i_end) issue(i0 + BP, buf ^ 1);
-        const uint16_t* qt = q_s[buf];
-        const uint16_t* gt = g_s[buf];
+        const uint16_t* qt = qg_s[buf];
+        const uint16_t* gt = qt + kBR * D;
 
-        // S = Q K^T and dP = dO V^T for this wave's 16 keys; lane: rows 16 rb + 4 lg + i
+        // S = Q K^T and dP = dO V^T for this wave's 16 keys; lane: rows 16 rb + 4 lg + i.
+        // Product pairs in k-step-major order (8 independent accumulators per k-step); each
+        // pair's Q and dO operands are read two pairs ahead, through a ring of three.
+        constexpr int NRD = RB * KS, NPV = RS * DB;
         f32x4 s[RB], dp[RB];
+        bf16x8 qa[3], ga[3];
+        auto rd_row = [&](int it) {
+            const int ks = it / RB, rb = it % RB;
+            const int e = (rb * 16 + l16) * D + ((ks * 4 + lg) ^ swz_row) * 8;
+            qa[it % 3] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + e));
+            ga[it % 3] = as_bf16x8(*reinterpret_cast<const u32x4*>(gt + e));
+        };
+        rd_row(0);
+        rd_row(1);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int e = (rb * 16 + l16) * D + ((ks * 4 + lg) ^ swz_row) * 8;
-                const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + e));
-                const bf16x8 ga = as_bf16x8(*reinterpret_cast<const u32x4*>(gt + e));
-                s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kop[ks], s[rb], 0, 0, 0);
-                dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vop[ks], dp[rb], 0, 0, 0);
-            }
+        for (int it = 0; it < NRD; ++it) {
+            const int ks = it / RB, rb = it % RB;
+            if (it + 2 < NRD) rd_row(it + 2);
+            const f32x4 s0 = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[rb];
+            const f32x4 d0 = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[rb];
+            s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[it % 3], kop[ks], s0, 0, 0, 0);
+            dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[it % 3], vop[ks], d0, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // transposed dO and Q operands of the second products (pair it: rows 32 (it / DB)..,
+        // d-block it % DB), read two pairs ahead through a ring of three; the first two go
+        // out before the softmax
+        bf16x8 gb[3], qb[3];
+        auto rd_tr = [&](int it) {
+            const int rs = it / DB, db = it % DB;
+            const int e = (32 * rs + 4 * lg + l16 / 4) * D +
+                          ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
+            gb[it % 3] = lds_read_tr2(gt + e, gt + e + 16 * D);
+            qb[it % 3] = lds_read_tr2(qt + e, qt + e + 16 * D);
+        };
+        rd_tr(0);
+        rd_tr(1);
         // P and dS as A operands of the row contraction (k = rows, order of vt_col). The
         // products of rows 0-31 (rs = 0) are issued with the P and dS values of rows 32-63
         // computed between them (scheduling barriers fix the order), so the wave's VALU work
@@ -434,21 +463,17 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         constexpr int PER = 8 / DB;   // values of rows 32-63 per d-block of rows 0-31
         static_assert(PER * DB == 8, "d-blocks per step");
 #pragma unroll
-        for (int rs = 0; rs < RS; ++rs)
+        for (int it = 0; it < NPV; ++it) {
+            const int rs = it / DB, db = it % DB;
+            if (it + 2 < NPV) rd_tr(it + 2);
+            dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rs], gb[it % 3], dv[db], 0, 0, 0);
+            dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[rs], qb[it % 3], dk[db], 0, 0, 0);
+            if (rs == 0) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int e = (32 * rs + 4 * lg + l16 / 4) * D +
-                              ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
-                const bf16x8 gb = lds_read_tr2(gt + e, gt + e + 16 * D);
-                const bf16x8 qb = lds_read_tr2(qt + e, qt + e + 16 * D);
-                dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rs], gb, dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[rs], qb, dk[db], 0, 0, 0);
-                if (rs == 0) {
-#pragma unroll
-                    for (int x = db * PER; x < (db + 1) * PER; ++x) pds(2 + x / 4, x % 4);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int x = db * PER; x < (db + 1) * PER; ++x) pds(2 + x / 4, x % 4);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // lane holds keys 16 w + 4 lg + i, dims 16 db + l16
@@ -471,9 +496,10 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_qtiles) {
     constexpr int BQ = kRows / G;
     constexpr int KS = D / 32, DB = D / 16, KB = kBN / 16, PVS = kBN / 32;
-    // K and V tiles: two buffers each, unpadded rows with chunk_swz, filled by direct loads
-    __shared__ __attribute__((aligned(1024))) uint16_t k_s[2][kBN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_s[2][kBN * D];
+    // K and V tiles: two buffers, each the K tile then the V tile (one base address serves
+    // both); unpadded rows with chunk_swz, filled by direct loads
+    constexpr int TB = kBN * D * 2;             // bytes of one tile
+    __shared__ __attribute__((aligned(1024))) uint16_t kv_s[2][2 * kBN * D];
 
     const int total = n_qtiles * a.Hkv * a.B;
     const int logical = xcd_logical(total);
@@ -522,9 +548,8 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
     // The next key tile's K and V rows go straight from memory into the other buffer
     // while this one is used (each wave issues its share; waited for at the top of the tile).
     const uint32_t k_lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&k_s[0][0]));
-    const uint32_t v_lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&v_s[0][0]));
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&kv_s[0][0]));
+    const uint32_t v_lds = k_lds + TB;
     constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBN / RPL / kWaves;
     static_assert(NPW * RPL * kWaves == kBN, "tile rows per wave");
     // key row r of a tile starts r Hkv D elements after the tile's first row; its chunks land
@@ -547,7 +572,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
         if (last >= kBN - 1) {
 #pragma unroll
             for (int x = 0; x < NPW; ++x) {
-                const uint32_t o = (uint32_t)(buf * kBN * D * 2 + (wave_u * NPW + x) * 1024);
+                const uint32_t o = (uint32_t)(buf * 2 * TB + (wave_u * NPW + x) * 1024);
                 lds_dma16(k_lds + o, kb_ + loff[x]);
                 lds_dma16(v_lds + o, vb_ + loff[x]);
             }
@@ -557,7 +582,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
             for (int x = 0; x < NPW; ++x) {
                 const int r = (wave_u * NPW + x) * RPL + lane / CPR;
                 const uint32_t e = lane_off(r, min(r, last));
-                const uint32_t o = (uint32_t)(buf * kBN * D * 2 + (wave_u * NPW + x) * 1024);
+                const uint32_t o = (uint32_t)(buf * 2 * TB + (wave_u * NPW + x) * 1024);
                 lds_dma16(k_lds + o, kb_ + e);
                 lds_dma16(v_lds + o, vb_ + e);
             }
@@ -579,30 +604,34 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
         __syncthreads();
         have = wk.next(seg, t0);
         if (have) issue(seg, t0, buf ^ 1);
-        const uint16_t* kt = k_s[buf];
-        const uint16_t* vt = v_s[buf];
+        const uint16_t* kt = kv_s[buf];
+        const uint16_t* vt = kt + kBN * D;
         buf ^= 1;
 
-        // S^T = K Q^T, dP^T = V dO^T; lane: keys 16 kb + 4 lg + i, row l16
+        // S^T = K Q^T, dP^T = V dO^T; lane: keys 16 kb + 4 lg + i, row l16. Each step's K
+        // and V operands (four products) are read one step ahead.
+        constexpr int NRD = KB * KS, NDQ = DB * PVS;
         f32x4 s[2][KB], dp[2][KB];
+        bf16x8 ka[2], va[2];
+        auto rd_row = [&](int it) {
+            const int kb = it / KS, ks = it % KS;
+            const int e = (kb * 16 + l16) * D + ((ks * 4 + lg) ^ swz_row) * 8;
+            ka[it % 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + e));
+            va[it % 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + e));
+        };
+        rd_row(0);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int it = 0; it < NRD; ++it) {
+            const int kb = it / KS, ks = it % KS;
+            if (it + 1 < NRD) rd_row(it + 1);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                dp[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 s0 = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[rb][kb];
+                const f32x4 d0 = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[rb][kb];
+                s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[it % 2], qop[rb][ks], s0, 0, 0, 0);
+                dp[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[it % 2], gop[rb][ks], d0, 0, 0, 0);
             }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int e = (kb * 16 + l16) * D + ((ks * 4 + lg) ^ swz_row) * 8;
-                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + e));
-                const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + e));
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[rb][ks], s[rb][kb], 0, 0, 0);
-                    dp[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gop[rb][ks], dp[rb][kb], 0, 0, 0);
-                }
-            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // dS^T as B operands (k = keys in vt_col order)
         if (!full) {
@@ -635,17 +664,26 @@ __global__ __launch_bounds__(kBlock, 2) void train_dq_kernel(TrainArgs a, int n_
                     const float p = __builtin_amdgcn_exp2f(s[rb][kb][i] * sc - lse2[rb]);
                     sb[rb][kb / 2][(kb & 1) * 4 + i] = (__bf16)(p * (dp[rb][kb][i] - di[rb]));
                 }
-        // dQ^T += K^T dS^T
+        __builtin_amdgcn_sched_barrier(0);
+        // dQ^T += K^T dS^T; the transposed K operands (pair it: d-block it / PVS, keys
+        // 32 (it % PVS)..) are read two pairs ahead, through a ring of three
+        bf16x8 kb3[3];
+        auto rd_tr = [&](int it) {
+            const int db = it / PVS, ps = it % PVS;
+            const int e = (32 * ps + 4 * lg + l16 / 4) * D +
+                          ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
+            kb3[it % 3] = lds_read_tr2(kt + e, kt + e + 16 * D);
+        };
+        rd_tr(0);
+        rd_tr(1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int ps = 0; ps < PVS; ++ps) {
-                const int e = (32 * ps + 4 * lg + l16 / 4) * D +
-                              ((db * 2 + (l16 % 4) / 2) ^ swz_tr) * 8 + (l16 & 1) * 4;
-                const bf16x8 ka = lds_read_tr2(kt + e, kt + e + 16 * D);
-                acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[0][ps], acc[0][db], 0, 0, 0);
-                acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sb[1][ps], acc[1][db], 0, 0, 0);
-            }
+        for (int it = 0; it < NDQ; ++it) {
+            const int db = it / PVS, ps = it % PVS;
+            if (it + 2 < NDQ) rd_tr(it + 2);
+            acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb3[it % 3], sb[0][ps], acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb3[it % 3], sb[1][ps], acc[1][db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
 #pragma unroll
