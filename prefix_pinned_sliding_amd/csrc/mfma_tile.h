@@ -149,27 +149,28 @@ __device__ __forceinline__ void tile_qk(f32x4 (&s)[2][kTileKeys / 16], const Sof
         s[0][kb] = f32x4{s0, s0, s0, s0};
         s[1][kb] = f32x4{s1, s1, s1, s1};
     }
-    // k-step outer: the 8 accumulators are independent within a step, and the next step's
-    // K operands are read while this step's products run
+    // k-step outer: the 8 accumulators are independent within a step. A step's K operands
+    // are read two steps ahead (a ring of three), so each read has two steps of products
+    // to land in; scheduling barriers keep that order.
     int ko[KS];
     k_operand_offsets<D>(ko, l16, lg);
-    bf16x8 ka[2][KB];
+    bf16x8 ka[3][KB];
+    auto kread = [&](int ks) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-        ka[0][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(k_s + kb * 16 * D + ko[0]));
+        for (int kb = 0; kb < KB; ++kb)
+            ka[ks % 3][kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(k_s + kb * 16 * D + ko[ks]));
+    };
+    kread(0);
+    if (KS > 1) kread(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                ka[(ks + 1) & 1][kb] = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(k_s + kb * 16 * D + ko[ks + 1]));
-        }
+        if (ks + 2 < KS) kread(ks + 2);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[0][ks], s[0][kb], 0, 0, 0);
-            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks & 1][kb], qop[1][ks], s[1][kb], 0, 0, 0);
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % 3][kb], qop[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % 3][kb], qop[1][ks], s[1][kb], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -377,9 +378,9 @@ __device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x
         s[1][kb] = f32x4{s1, s1, s1, s1};
     }
     // steps (half h, k-step ks) in order; each reads the K operands of its two key blocks,
-    // one step ahead
+    // two steps ahead (a ring of three)
     constexpr int NS = 2 * KS;
-    bf16x8 ka[2][2];
+    bf16x8 ka[3][2];
     int ko[KS];
     k_operand_offsets<D>(ko, l16, lg);
     auto kread = [&](int step, int j) -> bf16x8 {
@@ -388,18 +389,20 @@ __device__ __forceinline__ void tile_qk_exp(f32x4 (&s)[2][kTileKeys / 16], bf16x
     };
     ka[0][0] = kread(0, 0);
     ka[0][1] = kread(0, 1);
+    ka[1][0] = kread(1, 0);
+    ka[1][1] = kread(1, 1);
 #pragma unroll
     for (int step = 0; step < NS; ++step) {
         const int h = step / KS, ks = step % KS;
-        if (step + 1 < NS) {
-            ka[(step + 1) & 1][0] = kread(step + 1, 0);
-            ka[(step + 1) & 1][1] = kread(step + 1, 1);
+        if (step + 2 < NS) {
+            ka[(step + 2) % 3][0] = kread(step + 2, 0);
+            ka[(step + 2) % 3][1] = kread(step + 2, 1);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int kb = 2 * h + j;
-            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step & 1][j], qop[0][ks], s[0][kb], 0, 0, 0);
-            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step & 1][j], qop[1][ks], s[1][kb], 0, 0, 0);
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % 3][j], qop[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % 3][j], qop[1][ks], s[1][kb], 0, 0, 0);
         }
         if (h == 1) {
             // 16 / KS of the 16 exponentials of keys 0-31 per step of the second half
