@@ -57,6 +57,10 @@ CASES = [
     (2, 150, 8, 2, 64, 1, [3, 0], [150, 149]),
     (1, 300, 16, 2, 128, 300, [0], [300]),
     (2, 97, 8, 1, 128, 20, [97, 40], [97, 96]),
+    # many key tiles and query steps: 17 key tiles, window and prefix both longer than a
+    # tile, ragged lengths, G = 4 (D = 64) and G = 8 (D = 128)
+    (2, 1100, 16, 4, 64, 300, [100, 37], [1100, 777]),
+    (1, 900, 16, 2, 128, 200, [150], [900]),
 ]
 
 
