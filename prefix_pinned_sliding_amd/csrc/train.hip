@@ -199,22 +199,28 @@ __global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, in
 }
 
 // ---------------------------------------------------------------------------------------
-// Di = sum_d dO * O, one thread per (sequence, row, query head).
+// Di = sum_d dO * O per (sequence, row, query head): D / 8 lanes per row, each with one
+// 16-byte chunk of dO and of O, so a wave's loads cover whole consecutive rows; the partial
+// sums are added across the row's lanes.
 template <int D>
 __global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
-    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    if (idx >= (size_t)a.B * a.T * a.Hq) return;
-    const int i = (int)((idx / a.Hq) % a.T);
-    const int b = (int)(idx / ((size_t)a.Hq * a.T));
-    if (i >= a.len[b]) return;
-    const u32x4* g = reinterpret_cast<const u32x4*>(a.dout + idx * D);
-    const u32x4* o = reinterpret_cast<const u32x4*>(a.o + idx * D);
+    constexpr int LPR = D / 8;                       // lanes per row
+    static_assert(LPR == 8 || LPR == 16, "head dims 64 and 128");
+    const size_t rows = (size_t)a.B * a.T * a.Hq;
+    const size_t idx = (size_t)blockIdx.x * (kBlock / LPR) + threadIdx.x / LPR;
+    const int chunk = threadIdx.x % LPR;
+    bool ok = idx < rows;
+    if (ok) {
+        const int i = (int)((idx / a.Hq) % a.T);
+        const int b = (int)(idx / ((size_t)a.Hq * a.T));
+        ok = i < a.len[b];
+    }
     // A bf16 value is the high half of the float32 with the same bits, so each 32-bit word
     // holding two bf16 values gives its floats by a shift and a mask.
     float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4 x = g[c], y = o[c];
+    if (ok) {
+        const u32x4 x = reinterpret_cast<const u32x4*>(a.dout + idx * D)[chunk];
+        const u32x4 y = reinterpret_cast<const u32x4*>(a.o + idx * D)[chunk];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t xe = x[e], ye = y[e];
@@ -222,7 +228,9 @@ __global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
             acc += __uint_as_float(xe & 0xffff0000u) * __uint_as_float(ye & 0xffff0000u);
         }
     }
-    a.di[idx] = acc;
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
+    if (ok && chunk == 0) a.di[idx] = acc;
 }
 
 
@@ -714,8 +722,9 @@ hipError_t launch_train_g(const TrainArgs& a, bool backward, hipStream_t s) {
     const int q_total = n_qtiles * a.Hkv * a.B;
     const int q_grid = ((q_total + 7) / 8) * 8;
     const size_t rows = (size_t)a.B * a.T * a.Hq;
-    hipLaunchKernelGGL((train_rowdot_kernel<D>), dim3((unsigned)((rows + kBlock - 1) / kBlock)),
-                       dim3(kBlock), 0, s, a);
+    constexpr int rows_per_block = kBlock / (D / 8);
+    hipLaunchKernelGGL((train_rowdot_kernel<D>),
+                       dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(kBlock), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_ktiles = (a.T + kBN - 1) / kBN;
