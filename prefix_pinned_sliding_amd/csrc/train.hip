@@ -201,36 +201,50 @@ __global__ __launch_bounds__(kFwdBlock, 1) void train_fwd_kernel(TrainArgs a, in
 // ---------------------------------------------------------------------------------------
 // Di = sum_d dO * O per (sequence, row, query head): D / 8 lanes per row, each with one
 // 16-byte chunk of dO and of O, so a wave's loads cover whole consecutive rows; the partial
-// sums are added across the row's lanes.
+// sums are added across the row's lanes. Each lane group takes kRowdotRows rows, a block
+// apart, with all their loads issued first.
+constexpr int kRowdotRows = 4;
 template <int D>
 __global__ __launch_bounds__(kBlock) void train_rowdot_kernel(TrainArgs a) {
     constexpr int LPR = D / 8;                       // lanes per row
+    constexpr int RPB = kBlock / LPR;                // rows per block and pass
     static_assert(LPR == 8 || LPR == 16, "head dims 64 and 128");
     const size_t rows = (size_t)a.B * a.T * a.Hq;
-    const size_t idx = (size_t)blockIdx.x * (kBlock / LPR) + threadIdx.x / LPR;
     const int chunk = threadIdx.x % LPR;
-    bool ok = idx < rows;
-    if (ok) {
-        const int i = (int)((idx / a.Hq) % a.T);
-        const int b = (int)(idx / ((size_t)a.Hq * a.T));
-        ok = i < a.len[b];
-    }
-    // A bf16 value is the high half of the float32 with the same bits, so each 32-bit word
-    // holding two bf16 values gives its floats by a shift and a mask.
-    float acc = 0.f;
-    if (ok) {
-        const u32x4 x = reinterpret_cast<const u32x4*>(a.dout + idx * D)[chunk];
-        const u32x4 y = reinterpret_cast<const u32x4*>(a.o + idx * D)[chunk];
+    const size_t idx0 = (size_t)blockIdx.x * (RPB * kRowdotRows) + threadIdx.x / LPR;
+    bool ok[kRowdotRows];
+    u32x4 x[kRowdotRows], y[kRowdotRows];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t xe = x[e], ye = y[e];
-            acc += __uint_as_float(xe << 16) * __uint_as_float(ye << 16);
-            acc += __uint_as_float(xe & 0xffff0000u) * __uint_as_float(ye & 0xffff0000u);
+    for (int r = 0; r < kRowdotRows; ++r) {
+        const size_t idx = idx0 + (size_t)r * RPB;
+        ok[r] = idx < rows;
+        if (ok[r]) {
+            const int i = (int)((idx / a.Hq) % a.T);
+            const int b = (int)(idx / ((size_t)a.Hq * a.T));
+            ok[r] = i < a.len[b];
+        }
+        if (ok[r]) {
+            x[r] = reinterpret_cast<const u32x4*>(a.dout + idx * D)[chunk];
+            y[r] = reinterpret_cast<const u32x4*>(a.o + idx * D)[chunk];
         }
     }
 #pragma unroll
-    for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
-    if (ok && chunk == 0) a.di[idx] = acc;
+    for (int r = 0; r < kRowdotRows; ++r) {
+        // A bf16 value is the high half of the float32 with the same bits, so each 32-bit
+        // word holding two bf16 values gives its floats by a shift and a mask.
+        float acc = 0.f;
+        if (ok[r]) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t xe = x[r][e], ye = y[r][e];
+                acc += __uint_as_float(xe << 16) * __uint_as_float(ye << 16);
+                acc += __uint_as_float(xe & 0xffff0000u) * __uint_as_float(ye & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
+        if (ok[r] && chunk == 0) a.di[idx0 + (size_t)r * RPB] = acc;
+    }
 }
 
 
@@ -722,7 +736,7 @@ hipError_t launch_train_g(const TrainArgs& a, bool backward, hipStream_t s) {
     const int q_total = n_qtiles * a.Hkv * a.B;
     const int q_grid = ((q_total + 7) / 8) * 8;
     const size_t rows = (size_t)a.B * a.T * a.Hq;
-    constexpr int rows_per_block = kBlock / (D / 8);
+    constexpr int rows_per_block = kBlock / (D / 8) * kRowdotRows;
     hipLaunchKernelGGL((train_rowdot_kernel<D>),
                        dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(kBlock), 0, s, a);
     hipError_t e = hipGetLastError();
