@@ -12,8 +12,8 @@
 // masked tiles, two wave groups half a tile apart, three LDS buffers).
 // Backward, three kernels:
 //   rowdot  Di = sum_d dO * O per (row, head) (float32);
-//   dkdv    one workgroup per 64-key tile; each wave keeps its 16 keys' K and V in registers
-//           and walks the query tiles that see the tile: S = Q K^T, dP = dO V^T,
+//   dkdv    one 8-wave workgroup per 128-key tile; each wave keeps its 16 keys' K and V in
+//           registers and walks the query tiles that see the tile: S = Q K^T, dP = dO V^T,
 //           P = exp(S - lse), dS = P (dP - Di), dV += P^T dO, dK += dS^T Q;
 //   dq      one workgroup per 128-row query tile walking its visible key tiles:
 //           S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
@@ -268,10 +268,13 @@ __device__ __forceinline__ void lds_dma_wait() {
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (sequence, KV head, 64-key tile). Wave w owns keys
+// dK, dV: one workgroup per (sequence, KV head, kDkBN-key tile). Wave w owns keys
 // k0 + 16 w .. k0 + 16 w + 15. A query step is kBR rows = kBR / G positions x G heads.
+constexpr int kDkWaves = 8;                 // dK/dV workgroup: 16 keys per wave
+constexpr int kDkBlock = 64 * kDkWaves;
+constexpr int kDkBN = 16 * kDkWaves;        // keys per dK/dV workgroup
 template <int D, int G>
-__global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int n_ktiles) {
+__global__ __launch_bounds__(kDkBlock, 1) void train_dkdv_kernel(TrainArgs a, int n_ktiles) {
     constexpr int BP = kBR / G;                 // positions per query step
     constexpr int KS = D / 32, DB = D / 16, RB = kBR / 16, RS = kBR / 32;
     // Q and dO tiles: two buffers, each the Q tile then the dO tile (one base address serves
@@ -301,9 +304,9 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
     }
     const int h = bh % a.Hkv, b = bh / a.Hkv;
     const int len = a.len[b], P = a.pre[b], W = a.W;
-    const int k0 = kt * kBN;
+    const int k0 = kt * kDkBN;
     if (k0 >= len) return;
-    const int k1 = min(k0 + kBN, len);
+    const int k1 = min(k0 + kDkBN, len);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -338,8 +341,8 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(&qg_s[0][0]));
     const uint32_t g_lds = q_lds + TB;
     float lse_r = 0.f, di_r = 0.f;
-    constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBR / RPL / kWaves;
-    static_assert(NPW * RPL * kWaves == kBR, "tile rows per wave");
+    constexpr int CPR = D / 8, RPL = 64 / CPR, NPW = kBR / RPL / kDkWaves;
+    static_assert(NPW * RPL * kDkWaves == kBR, "tile rows per wave");
     // row r of a step (position r / G, head r % G) starts ((r / G) Hq + r % G) D elements
     // after the step's first row; its chunks land swizzled by r. This lane's rows of a full
     // step, once: r = (NPW wave + x) RPL + lane / CPR.
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(kBlock, 2) void train_dkdv_kernel(TrainArgs a, int 
     for (int i0 = k0; i0 < i_end; i0 += BP, buf ^= 1) {
         const int i1 = min(i0 + BP, len);             // positions [i0, i1)
         const int last = (i1 - i0) * G - 1;            // last valid row of the step
-        const bool full = (i1 - i0 == BP) && (k1 - k0 == kBN) && (k1 - 1 <= i0) &&
+        const bool full = (i1 - i0 == BP) && (k1 - k0 == kDkBN) && (k1 - 1 <= i0) &&
                           (k1 - 1 < P || k0 >= (i1 - 1) - W + 1);
         lds_dma_wait<0>();
         if (tid < kBR) {
@@ -741,10 +744,10 @@ hipError_t launch_train_g(const TrainArgs& a, bool backward, hipStream_t s) {
                        dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(kBlock), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_ktiles = (a.T + kBN - 1) / kBN;
+    const int n_ktiles = (a.T + kDkBN - 1) / kDkBN;
     const int k_total = n_ktiles * a.Hkv * a.B;
-    hipLaunchKernelGGL((train_dkdv_kernel<D, G>), dim3(((k_total + 7) / 8) * 8), dim3(kBlock), 0, s,
-                       a, n_ktiles);
+    hipLaunchKernelGGL((train_dkdv_kernel<D, G>), dim3(((k_total + 7) / 8) * 8), dim3(kDkBlock), 0,
+                       s, a, n_ktiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((train_dq_kernel<D, G>), dim3(q_grid), dim3(kBlock), 0, s, a, n_qtiles);
