@@ -79,7 +79,9 @@ typedef struct {
     int32_t head_dim;    /* D: 64 or 128 */
     int32_t prefix_max;  /* P_max >= 0: largest pinned-prefix length any sequence may use */
     int32_t window;      /* W >= 1: window length (the largest psa_seq_set_window accepts);
-                            prefix_max + window <= 2^30, and W < 2^24 when max_chunk > 0 */
+                            prefix_max + window <= 2^30, n_kv_heads * (ceil((max(prefix_max,
+                            shared_prefix_max) + window) / 128) + 1) < 2^24, and W < 2^24
+                            when max_chunk > 0 */
     int32_t dtype;       /* PSA_BF16 or PSA_F32 (storage, inputs and outputs) */
     int32_t max_chunk;   /* largest prefill chunk C (0: psa_prefill_attn unavailable);
                             C * n_kv_heads * head_dim < 2^32 */

@@ -10,8 +10,13 @@
 // last one of a split (masked per key). Softmax order does not matter, so a full ring is
 // walked from slot 0 rather than in age order.
 //
-// Work split: one workgroup (4 waves) per (split, kv head, sequence). A split is a
-// contiguous run of `split_tokens` entries of the concatenated [prefix | ring] list.
+// Work split: one workgroup (4 waves) per (kv head, split, sequence); grid x holds
+// (split, head) pairs with the head fastest, grid y the sequences in the order array.
+// Consecutive workgroups go to the eight XCDs in turn, so with H_kv = 8 each
+// XCD takes one head of every split and the XCDs get equal work whatever the split count
+// (with the split fastest, an even count put every sequence's first, full split on half of
+// them). A split is a contiguous run of `split_tokens` entries of the concatenated
+// [prefix | ring] list.
 // Within a wave, LPK lanes share one key (each holds D / LPK of its elements, 16-byte
 // loads), so a wave covers 64 / LPK keys per load; the G query heads of the kv head
 // reuse every K/V element loaded. Logits are reduced over the LPK lanes with DPP, the
@@ -105,9 +110,9 @@ __device__ __forceinline__ float row_group_sum(float x) {
 #ifndef PSA_DECODE_LPK_G2
 #define PSA_DECODE_LPK_G2 8      // lanes per key when a KV head serves one or two query heads
 #endif
-#ifndef PSA_DECODE_PIPELINE
-#define PSA_DECODE_PIPELINE 1    // 1: load the next iteration's K/V before computing this one
-#endif
+#ifndef PSA_DECODE_RING
+#define PSA_DECODE_RING 2        // K/V tiles per wave in the register ring (one in flight per
+#endif                           // tile computed)
 
 template <int DT, int D, int LPK, int U>
 struct KVTile {
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     static_assert(CPL >= 1 && CPR % LPK == 0, "lane layout");
     using Tile = KVTile<DT, D, LPK, U>;
 
-    const int split = blockIdx.x, h = blockIdx.y, b = c.order[blockIdx.z];
+    const int h = blockIdx.x % c.Hkv, split = blockIdx.x / c.Hkv, b = c.order[blockIdx.y];
     const bool fused = k_new != nullptr;
     const int n = len_cur[b] + (fused ? 1 : 0);
     const SeqView sv = seq_view(c, b, n);
@@ -246,9 +251,9 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
     // The owner appends this head's new token (position n - 1) as append_kernel does, on
     // the last wave (the query set-up below runs on the first ones), then makes the stores
     // visible to the workgroup's loads: a fence, and a barrier before any load that may
-    // reach the new entry. When the first batch of loads (entries [i0, i0 + STEP), the last
-    // one repeated past i1) cannot reach it, those loads go out first and the barrier after
-    // the query set-up serves; otherwise the append and a barrier come first.
+    // reach the new entry. When the ring's first loads (entries [i0, i0 + R * STEP), any
+    // past i1 read as i1 - 1) cannot reach it, those loads go out first and the barrier
+    // after the query set-up serves; otherwise the append and a barrier come first.
     auto append_new = [&](bool barrier) {
         constexpr int H = D / 2;
         const int t = tid - (kBlock - H);
@@ -274,13 +279,15 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
         }
         if (barrier) __syncthreads();
     };
-    const bool append_first = split == owner && i_new < i0 + STEP;
+    constexpr int R = PSA_DECODE_RING;
+    const bool append_first = split == owner && i_new < i0 + R * STEP;
     if (append_first) append_new(true);
 
-    // First K/V loads go out before the query set-up so that latency overlaps.
-    int base_i = i0 + wave * KPW * U;
-    Tile nxt;
-    if (base_i < i1) load(nxt, base_i);
+    // The ring's first K/V loads go out before the query set-up so that latency overlaps.
+    const int base_i = i0 + wave * KPW * U;
+    Tile ring[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load(ring[r], base_i + r * STEP);
     if (split == owner && !append_first) append_new(false);   // barrier: after the query set-up
 
     {
@@ -315,12 +322,8 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
         for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
 
-    while (base_i < i1) {
-        Tile cur = nxt;
-        const int cur_i = base_i;
-        base_i += STEP;
-        if (PSA_DECODE_PIPELINE && base_i < i1) load(nxt, base_i);
-
+    // One tile of the wave's keys: logits, running max, then the value accumulation.
+    auto consume = [&](const Tile& cur, const int cur_i) {
         float s[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -364,7 +367,19 @@ __global__ __launch_bounds__(kBlock) void decode_partial_kernel(DevCache c,
                 for (int e = 0; e < EPL; ++e) acc[g][e] += pr * vf[e];
             }
         }
-        if (!PSA_DECODE_PIPELINE && base_i < i1) load(nxt, base_i);
+    };
+    // Register ring of R tiles, unrolled so that no tile is copied: each tile is consumed
+    // and then reloaded R iterations ahead, so the compiler waits only for the tile about
+    // to be used (a rotation by copies would wait for every load in flight). Loads past i1
+    // repeat entry i1 - 1 and are never consumed.
+    int cur_i = base_i;
+    while (cur_i < i1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (cur_i < i1) consume(ring[r], cur_i);
+            load(ring[r], cur_i + R * STEP);
+            cur_i += STEP;
+        }
     }
 
     // Combine: lane groups in a row share m, so sum them; rows and waves go through LDS.
@@ -450,7 +465,7 @@ hipError_t launch_partial_g(const DevCache& c, const void* q, int split_tokens, 
     constexpr int CPR = D / (16 / (int)sizeof(typename Elem<DT>::T));
     constexpr int PREF = G <= 2 ? PSA_DECODE_LPK_G2 : (G == 4 ? 8 : 16);
     constexpr int LPK = PREF < CPR ? PREF : CPR;
-    const dim3 grid(grid_splits, c.Hkv, c.B);
+    const dim3 grid(c.Hkv * grid_splits, c.B);
     if (c.Bs > 0)
         hipLaunchKernelGGL((decode_partial_kernel<DT, D, G, LPK, true>), grid, dim3(kBlock), 0, s, c,
                            (const T*)q, split_tokens, c.len[cur], (const T*)k_new, (const T*)v_new,

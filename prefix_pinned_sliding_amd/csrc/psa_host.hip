@@ -50,7 +50,7 @@ struct psa_cache {
     std::vector<int32_t> attached; // sequences attached to each pool entry
     std::vector<int32_t> btab;     // paged: host copy of the block table [B][NBT]
     std::vector<int32_t> free_blk; // paged: unused physical blocks (a stack)
-    std::vector<int32_t> order;    // decode workgroup order on the device (grid z -> sequence)
+    std::vector<int32_t> order;    // decode workgroup order on the device (grid y -> sequence)
     int32_t split_tokens;          // 0 = automatic
     int resident_wgs;              // decode workgroups resident at once (0 = not yet queried)
     bool profiling;
@@ -66,8 +66,8 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
         *why = w;
         return false;
     };
-    // The decode launch puts sequences on grid z and KV heads on grid y, the merge launch
-    // sequences on grid y: both dimensions hold at most 65535.
+    // The decode and merge launches put sequences on grid y: at most 65535. The decode
+    // launch's grid x holds (split, KV head) pairs (checked below).
     if (d.max_batch < 1 || d.max_batch > kMaxGridYZ) return bad("max_batch must be in [1, 65535]");
     if (d.n_kv_heads < 1 || d.n_kv_heads > kMaxGridYZ) return bad("n_kv_heads must be in [1, 65535]");
     if (d.n_q_heads < 1 || d.n_q_heads % d.n_kv_heads != 0)
@@ -119,6 +119,9 @@ bool compute_layout(const psa_cache_desc& d, Layout* L, const char** why) {
     // entries; RESET splits the prefix and the window separately: one more split at most.
     const int64_t seen = (int64_t)std::max(d.prefix_max, d.shared_prefix_max) + d.window;
     const int64_t max_splits = (seen + kSplitGranule - 1) / kSplitGranule + 1;
+    if ((int64_t)d.n_kv_heads * max_splits >= (1 << 24))
+        return bad("n_kv_heads * decode splits must be < 2^24 (splits: one per 128 entries of "
+                   "max(prefix_max, shared_prefix_max) + window, plus one)");
     const size_t A = 256;
     size_t off = 0;
     const size_t kv_rows = d.block_size ? (size_t)n_blocks * Hkv * (size_t)d.block_size
@@ -278,7 +281,7 @@ int plan_decode(psa_cache* c, int* split_len, int* grid_splits) {
     return PSA_OK;
 }
 
-// Decode workgroups go out sequence by sequence in the device order array (grid z); with
+// Decode workgroups go out sequence by sequence in the device order array (grid y); with
 // sequences of different lengths, the longest first, so the short ones fill the end of
 // the launch instead of a long one running alone. Sequences are ranked by visible entries
 // in units of kSplitGranule (ties in index order), so steady decoding, which adds one

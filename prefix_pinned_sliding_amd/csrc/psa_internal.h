@@ -28,7 +28,7 @@ struct DevCache {
     int32_t* npin;       // [B] pinned entries once the prefix is complete (P_b + promoted)
     int32_t* wfloor;     // [B] no window entry is older than this position
     int32_t* wlen;       // [B] the sequence's window length w_b (<= W)
-    int32_t* order;      // [B] decode workgroup order: grid index z -> sequence (longest first)
+    int32_t* order;      // [B] decode workgroup order: grid index y -> sequence (longest first)
     double* inv_freq;    // [D/2] theta_i
     float* part_o;       // [B][Hq][max_splits][D] unnormalised split outputs
     float* part_ml;      // [B][Hq][max_splits][2] split max (log2 domain) and sum
