@@ -96,6 +96,22 @@ def test_shapes_beyond_the_kernels_addressing_are_rejected(psa, bad):
     assert psa.lib.psa_last_error().decode() != ""
 
 
+def test_decode_grid_bound(psa):
+    # the decode grid's x dimension holds n_kv_heads * splits workgroups of 256 threads:
+    # n_kv_heads * (ceil(seen / 128) + 1) must stay below 2^24
+    ok = good_desc(psa, max_batch=1, n_q_heads=1, n_kv_heads=1, prefix_max=0, window=1 << 28,
+                   max_chunk=0)
+    assert psa.cache_layout(ok).max_splits == (1 << 21) + 1
+    d = good_desc(psa, max_batch=1, n_q_heads=8, n_kv_heads=8, prefix_max=0, window=1 << 28,
+                  max_chunk=0)
+    assert psa.lib.psa_cache_bytes(ctypes.byref(d)) == 0
+    assert "decode splits" in psa.lib.psa_last_error().decode()
+    # just inside: 8 * (2^21 - 2 + 1) < 2^24
+    edge = good_desc(psa, max_batch=1, n_q_heads=8, n_kv_heads=8, prefix_max=0,
+                     window=((1 << 21) - 2) * 128, max_chunk=0)
+    assert psa.cache_layout(edge).max_splits == (1 << 21) - 1
+
+
 def test_long_window_is_accepted_without_prefill(psa):
     # the 24-bit row bound belongs to chunked prefill only
     d = good_desc(psa, max_batch=1, n_q_heads=8, n_kv_heads=8, prefix_max=0, window=1 << 24,
