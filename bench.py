@@ -625,6 +625,8 @@ def main():
         result["decode_p512_w16384"] = bench_decode_config("decode_p512_w16384", 10, 50)
         print("[bench] ragged decode B=256", file=sys.stderr, flush=True)
         result["ragged_decode"] = bench_decode_config("ragged_decode", 0, 64)
+        print("[bench] decode with a window length per sequence", file=sys.stderr, flush=True)
+        result["decode_ragged_window"] = bench_decode_config("decode_ragged_window", 10, 50)
         print("[bench] flat in t", file=sys.stderr, flush=True)
         result["flat_in_t"] = bench_flat_in_t()
 
